@@ -1,0 +1,111 @@
+/*
+ * Plain fp64 CPU oracle for exact attention:  O = softmax(scale * Q K^T) V,
+ * plus the per-row log-sum-exp.  TEST INFRASTRUCTURE ONLY: the test-suite,
+ * the smoke check and the benchmark's CPU-baseline leg call it; the GPU
+ * library never does, and the two share no code.
+ *
+ * What it computes follows the three-step definition of standard attention
+ * (zzszmyf.github.io notes "FlashAttention 原理是什么", section 2: S = QK^T,
+ * P = softmax(S), O = PV; aiqz.cc Flash Attention IO article, section
+ * 标准注意力瓶颈) with the max-subtracted row softmax of the cf-1.com
+ * FlashAttention write-up, section 3.1 (m = max x, l = sum exp(x - m),
+ * softmax = exp(x - m) / l).  Rows are handled one at a time, so no N x N
+ * buffer is formed; nothing is tiled or merged online.
+ *
+ * Readings of what the pages leave open:
+ *   - S is scaled by `scale` before the softmax (the pages' demo omits it).
+ *   - causal: key j takes part in row i iff j <= i (square problem); a masked
+ *     key is excluded outright.
+ *   - LSE_i = m_i + ln(l_i) over the scaled, masked scores (natural log).
+ * Inputs are float32 arrays (bf16 data is widened exactly before the call);
+ * every product and sum is carried in IEEE double, no fast-math.
+ */
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+#include <stdlib.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* One query row: flat row index r = (b*H + h)*N + i.  Writes d values of O
+ * and one LSE.  `s` is a caller-provided scratch row of N doubles. */
+static void oracle_row(const float* q, const float* k, const float* v,
+                       int64_t H, int64_t N, int64_t d, double scale,
+                       int causal, int64_t r, double* s, double* o_row,
+                       double* lse_out) {
+  const int64_t bh = r / N;          /* (b*H + h) */
+  const int64_t i = r % N;           /* query position inside the head */
+  const float* qi = q + r * d;
+  const float* kh = k + bh * N * d;
+  const float* vh = v + bh * N * d;
+  const int64_t nkeys = causal ? (i + 1) : N;   /* keys j with j <= i */
+  (void)H;
+
+  /* step 1: scores s_j = scale * <q_i, k_j> */
+  double m = -INFINITY;
+  for (int64_t j = 0; j < nkeys; ++j) {
+    const float* kj = kh + j * d;
+    double dot = 0.0;
+    for (int64_t c = 0; c < d; ++c) dot += (double)qi[c] * (double)kj[c];
+    s[j] = scale * dot;
+    if (s[j] > m) m = s[j];
+  }
+  /* step 2: row softmax with the row max subtracted */
+  double l = 0.0;
+  for (int64_t j = 0; j < nkeys; ++j) {
+    s[j] = exp(s[j] - m);
+    l += s[j];
+  }
+  /* step 3: O_i = sum_j p_j v_j / l */
+  for (int64_t c = 0; c < d; ++c) o_row[c] = 0.0;
+  for (int64_t j = 0; j < nkeys; ++j) {
+    const float* vj = vh + j * d;
+    const double p = s[j];
+    for (int64_t c = 0; c < d; ++c) o_row[c] += p * (double)vj[c];
+  }
+  for (int64_t c = 0; c < d; ++c) o_row[c] /= l;
+  *lse_out = m + log(l);
+}
+
+/* Attention over the rows listed in `rows` (flat indices into [B,H,N]);
+ * rows == NULL means every row, in order.  O is [nrows, d], LSE [nrows].
+ * Returns 0 on success, 1 on a bad argument, 2 if scratch allocation fails. */
+int oracle_attn_f64(const float* q, const float* k, const float* v,
+                    int64_t B, int64_t H, int64_t N, int64_t d, double scale,
+                    int causal, const int64_t* rows, int64_t nrows,
+                    double* O, double* LSE) {
+  if (!q || !k || !v || !O || !LSE || B < 1 || H < 1 || N < 1 || d < 1)
+    return 1;
+  const int64_t total = B * H * N;
+  if (!rows) nrows = total;
+  if (nrows < 0) return 1;
+  for (int64_t t = 0; t < nrows && rows; ++t)
+    if (rows[t] < 0 || rows[t] >= total) return 1;
+  int failed = 0;
+#pragma omp parallel
+  {
+    double* s = (double*)malloc(sizeof(double) * (size_t)N);
+    if (!s) {
+#pragma omp atomic write
+      failed = 1;
+    } else {
+#pragma omp for schedule(dynamic, 16)
+      for (int64_t t = 0; t < nrows; ++t) {
+        const int64_t r = rows ? rows[t] : t;
+        oracle_row(q, k, v, H, N, d, scale, causal, r, s, O + t * d, LSE + t);
+      }
+      free(s);
+    }
+  }
+  return failed ? 2 : 0;
+}
+
+/* Threads the OpenMP runtime will use for the next parallel region. */
+int oracle_max_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
