@@ -1,0 +1,89 @@
+/*
+ * fa_fwd.h -- fused exact-attention forward pass for AMD MI355X (gfx950).
+ *
+ * Computes, for every batch b, head h and query row i,
+ *
+ *     O[b,h,i,:]  = sum_j softmax_j(scale * <q_i, k_j>) * v_j
+ *     LSE[b,h,i]  = log( sum_j exp(scale * <q_i, k_j>) )          (natural log)
+ *
+ * with j over all keys, or over j <= i when `causal` is 1.  The problem is the
+ * one stated by the zzszmyf.github.io notes "FlashAttention 原理是什么？为什么又省
+ * 显存又快": Q, K, V of N x d per head in device memory, exact
+ * softmax(Q K^T) V returned with O(N) extra memory (section 7.2, Theorem 1),
+ * with the per-row softmax statistics kept for a recomputing backward pass
+ * (section 6), here folded into one log-sum-exp per row.  The N x N score and
+ * probability matrices never reach device memory: K/V are streamed tile by
+ * tile and merged with a running row max and row sum (aiqz.cc Flash
+ * Attention IO article, section 在线Softmax算法).
+ *
+ * Layout: every tensor is dense row-major [B, H, N, d] (d fastest); LSE is
+ * [B, H, N] float32.  O has the input element type.
+ *
+ * Ownership: the caller allocates and owns every buffer.  The library
+ * allocates nothing, keeps no state between calls and is thread-safe.  O and
+ * LSE must not overlap Q, K, V or each other.
+ *
+ * Errors: argument errors are detected on the host before any HIP call and
+ * returned synchronously (no work is queued).  A failed kernel launch returns
+ * FA_ERR_HIP.  The work itself runs asynchronously on `stream` (0 = the null
+ * stream); a fault during execution surfaces at the caller's next
+ * synchronisation of that stream.
+ */
+#ifndef FA_FWD_H
+#define FA_FWD_H
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum fa_status {
+  FA_OK = 0,
+  FA_ERR_NULL = 1,           /* a required pointer is NULL                     */
+  FA_ERR_SHAPE = 2,          /* B, H or N < 1, or the problem is too large     */
+  FA_ERR_UNSUPPORTED_D = 3,  /* head dimension other than 64 or 128            */
+  FA_ERR_SCALE = 4,          /* scale not finite or not > 0                    */
+  FA_ERR_ALIGN = 5,          /* a pointer is not 16-byte aligned               */
+  FA_ERR_HIP = 6,            /* the HIP runtime refused the launch             */
+  FA_ERR_CAUSAL = 7,         /* causal flag other than 0 or 1                  */
+  FA_ERR_ALIAS = 8           /* O or LSE overlaps an input or each other       */
+};
+
+/*
+ * bfloat16 attention forward: the hot path.
+ *   q, k, v : device pointers, [B,H,N,d] bfloat16 (raw 16-bit storage).
+ *   o       : device pointer, [B,H,N,d] bfloat16, written (round to nearest
+ *             even from the fp32 result).
+ *   lse     : device pointer, [B,H,N] float32, written.
+ *   B, H, N : batch, heads, sequence length (N >= 1; any N, no tile multiple
+ *             needed).  B*H*N*d must stay below 2^40 elements.
+ *   d       : head dimension, 64 or 128.
+ *   scale   : multiplier of Q K^T before the softmax, finite and > 0
+ *             (usually 1/sqrt(d)).
+ *   causal  : 1 -> key j attends to query i only when j <= i; 0 -> all keys.
+ *   stream  : HIP stream the kernel is queued on.
+ * Products are taken on bf16 matrix cores with fp32 accumulation; the
+ * softmax statistics, the rescaling and the final division are fp32.
+ * Returns an fa_status.
+ */
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+           int B, int H, int N, int d, float scale, int causal,
+           hipStream_t stream);
+
+/*
+ * float32 twin of fa_fwd: q, k, v, o are [B,H,N,d] float32 and every
+ * product, sum and exponential is fp32.  Same argument rules and errors.
+ */
+int fa_fwd_f32(const float* q, const float* k, const float* v, float* o,
+               float* lse, int B, int H, int N, int d, float scale,
+               int causal, hipStream_t stream);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char* fa_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_FWD_H */

@@ -1,0 +1,113 @@
+"""ctypes binding of libfa_fwd.so (declared in include/fa_fwd.h).
+
+Argument marshalling only: every step of the attention forward pass runs in
+the library's HIP kernels.  There is no fallback: if the library is missing
+or cannot be loaded, every call raises.
+
+Low level (same names and arguments as the C functions, raw pointers):
+    fa_fwd(q, k, v, o, lse, B, H, N, d, scale, causal, stream) -> status
+    fa_fwd_f32(...)                                            -> status
+    fa_strerror(status)                                        -> str
+High level (torch tensors on a ROCm device):
+    fwd(q, k, v, scale=None, causal=False, out=None, lse=None) -> (o, lse)
+"""
+import ctypes
+import math
+import os
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa_fwd.so")
+
+FA_OK = 0
+FA_ERR_NULL = 1
+FA_ERR_SHAPE = 2
+FA_ERR_UNSUPPORTED_D = 3
+FA_ERR_SCALE = 4
+FA_ERR_ALIGN = 5
+FA_ERR_HIP = 6
+FA_ERR_CAUSAL = 7
+FA_ERR_ALIAS = 8
+
+EXPORTED = ("fa_fwd", "fa_fwd_f32", "fa_strerror")
+
+_lib = None
+
+
+class FaError(RuntimeError):
+    def __init__(self, status, what):
+        super().__init__("%s failed: %s (status %d)" % (what, fa_strerror(status), status))
+        self.status = status
+
+
+def load():
+    """Load libfa_fwd.so once; raise if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            "libfa_fwd.so not found at %s; build it with "
+            "`python -m io_aware_softmax_fwd_amd.build`" % LIB_PATH)
+    lib = ctypes.CDLL(LIB_PATH)
+    args = [ctypes.c_void_p] * 5 + [ctypes.c_int] * 4 + [ctypes.c_float, ctypes.c_int, ctypes.c_void_p]
+    for name in ("fa_fwd", "fa_fwd_f32"):
+        f = getattr(lib, name)
+        f.restype = ctypes.c_int
+        f.argtypes = args
+    lib.fa_strerror.restype = ctypes.c_char_p
+    lib.fa_strerror.argtypes = [ctypes.c_int]
+    _lib = lib
+    return lib
+
+
+def fa_fwd(q, k, v, o, lse, B, H, N, d, scale, causal, stream):
+    return load().fa_fwd(q, k, v, o, lse, B, H, N, d, scale, causal, stream)
+
+
+def fa_fwd_f32(q, k, v, o, lse, B, H, N, d, scale, causal, stream):
+    return load().fa_fwd_f32(q, k, v, o, lse, B, H, N, d, scale, causal, stream)
+
+
+def fa_strerror(status):
+    return load().fa_strerror(int(status)).decode()
+
+
+def fwd(q, k, v, scale=None, causal=False, out=None, lse=None, stream=None):
+    """Attention forward of torch tensors q, k, v [B,H,N,d] (bf16 or fp32,
+    contiguous, on the GPU).  Queues the kernel on `stream` (default: torch's
+    current stream) and returns (o, lse); o has q's dtype, lse is fp32 [B,H,N].
+    """
+    import torch
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor):
+            raise TypeError("%s must be a torch.Tensor" % name)
+        if t.device.type != "cuda":
+            raise ValueError("%s must live on the GPU" % name)
+        if not t.is_contiguous():
+            raise ValueError("%s must be contiguous" % name)
+        if t.dim() != 4:
+            raise ValueError("%s must be [B, H, N, d]" % name)
+    if q.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("q must be bfloat16 or float32")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k, v must share one dtype")
+    if k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k, v must share one shape")
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    if out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor like q")
+    if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 [B, H, N] tensor")
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    f = fa_fwd if q.dtype == torch.bfloat16 else fa_fwd_f32
+    st = f(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+           B, H, N, d, float(scale), int(bool(causal)), stream)
+    if st != FA_OK:
+        raise FaError(st, f.__name__)
+    return out, lse

@@ -1,0 +1,79 @@
+// C entry points of libfa_fwd.so (declared in include/fa_fwd.h).
+//
+// Every argument is checked on the host before any HIP call, so a bad call
+// returns its status without touching the device (and can be tested on a
+// machine with no GPU).  Valid calls are forwarded to the kernel launchers.
+#include <math.h>
+#include <stdint.h>
+
+#include "fa_fwd.h"
+#include "fa_internal.h"
+
+namespace {
+
+// Largest supported problem: element offsets stay far inside int64 and the
+// 1-D grid (query tiles x heads) inside 2^31 workgroups.
+constexpr int64_t kMaxElems = int64_t(1) << 40;
+
+bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
+
+bool overlap(const void* a, int64_t a_bytes, const void* b, int64_t b_bytes) {
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+  return a0 < b0 + (uintptr_t)b_bytes && b0 < a0 + (uintptr_t)a_bytes;
+}
+
+int validate(const void* q, const void* k, const void* v, const void* o, const float* lse,
+             int B, int H, int N, int d, float scale, int causal, int elem_bytes) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+  if (B < 1 || H < 1 || N < 1) return FA_ERR_SHAPE;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED_D;
+  const int64_t rows = (int64_t)B * H * N;
+  if (rows * d >= kMaxElems) return FA_ERR_SHAPE;
+  if (!(scale > 0.f) || !isfinite(scale)) return FA_ERR_SCALE;
+  if (causal != 0 && causal != 1) return FA_ERR_CAUSAL;
+  if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(o) || misaligned(lse))
+    return FA_ERR_ALIGN;
+  const int64_t tb = rows * d * elem_bytes, lb = rows * 4;
+  if (overlap(o, tb, q, tb) || overlap(o, tb, k, tb) || overlap(o, tb, v, tb) ||
+      overlap(lse, lb, q, tb) || overlap(lse, lb, k, tb) || overlap(lse, lb, v, tb) ||
+      overlap(lse, lb, o, tb))
+    return FA_ERR_ALIAS;
+  return FA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N,
+           int d, float scale, int causal, hipStream_t stream) {
+  const int st = validate(q, k, v, o, lse, B, H, N, d, scale, causal, 2);
+  if (st != FA_OK) return st;
+  const fa::Problem p{q, k, v, o, lse, B, H, N, d, scale, causal};
+  return fa::launch_fwd_bf16(p, stream) == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B, int H,
+               int N, int d, float scale, int causal, hipStream_t stream) {
+  const int st = validate(q, k, v, o, lse, B, H, N, d, scale, causal, 4);
+  if (st != FA_OK) return st;
+  const fa::Problem p{q, k, v, o, lse, B, H, N, d, scale, causal};
+  return fa::launch_fwd_f32(p, stream) == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+const char* fa_strerror(int status) {
+  switch (status) {
+    case FA_OK: return "success";
+    case FA_ERR_NULL: return "a required pointer is NULL";
+    case FA_ERR_SHAPE: return "B, H and N must be >= 1 and B*H*N*d below 2^40";
+    case FA_ERR_UNSUPPORTED_D: return "head dimension must be 64 or 128";
+    case FA_ERR_SCALE: return "scale must be finite and > 0";
+    case FA_ERR_ALIGN: return "pointers must be 16-byte aligned";
+    case FA_ERR_HIP: return "the HIP runtime rejected the kernel launch";
+    case FA_ERR_CAUSAL: return "causal must be 0 or 1";
+    case FA_ERR_ALIAS: return "O or LSE overlaps an input or each other";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,89 @@
+"""The C boundary on a host without a GPU: the library loads, exports every
+function include/fa_fwd.h declares, and rejects bad arguments on the host
+before any HIP call (no launch happens, so fake device addresses are safe)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import io_aware_softmax_fwd_amd as fa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa_fwd.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_binding_names():
+    assert _declared() == sorted(fa.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    fa.load()
+    out = subprocess.run(["nm", "-D", "--defined-only", fa.binding.LIB_PATH],
+                         capture_output=True, text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    for name in _declared():
+        assert name in exported, name
+        assert hasattr(fa.load(), name)
+
+
+def test_status_enum_matches_header():
+    text = open(HEADER).read()
+    for name, val in re.findall(r"(FA_\w+)\s*=\s*(\d+)", text):
+        assert getattr(fa, name) == int(val), name
+
+
+A = 0x10000          # fake, 16-byte aligned "device" addresses; never touched
+MB = 1 << 20
+
+
+def _call(fn, **kw):
+    args = dict(q=A, k=A + 8 * MB, v=A + 16 * MB, o=A + 24 * MB, lse=A + 32 * MB,
+                B=1, H=2, N=64, d=64, scale=0.125, causal=0, stream=None)
+    args.update(kw)
+    return fn(args["q"], args["k"], args["v"], args["o"], args["lse"], args["B"], args["H"],
+              args["N"], args["d"], args["scale"], args["causal"], args["stream"])
+
+
+@pytest.mark.parametrize("fn", [fa.fa_fwd, fa.fa_fwd_f32])
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), fa.FA_ERR_NULL), (dict(k=None), fa.FA_ERR_NULL),
+    (dict(v=None), fa.FA_ERR_NULL), (dict(o=None), fa.FA_ERR_NULL),
+    (dict(lse=None), fa.FA_ERR_NULL),
+    (dict(B=0), fa.FA_ERR_SHAPE), (dict(H=-1), fa.FA_ERR_SHAPE), (dict(N=0), fa.FA_ERR_SHAPE),
+    (dict(B=1 << 20, H=1 << 10, N=1 << 10, d=128), fa.FA_ERR_SHAPE),
+    (dict(d=32), fa.FA_ERR_UNSUPPORTED_D), (dict(d=96), fa.FA_ERR_UNSUPPORTED_D),
+    (dict(d=256), fa.FA_ERR_UNSUPPORTED_D),
+    (dict(scale=0.0), fa.FA_ERR_SCALE), (dict(scale=-0.5), fa.FA_ERR_SCALE),
+    (dict(scale=float("inf")), fa.FA_ERR_SCALE), (dict(scale=float("nan")), fa.FA_ERR_SCALE),
+    (dict(causal=2), fa.FA_ERR_CAUSAL), (dict(causal=-1), fa.FA_ERR_CAUSAL),
+    (dict(q=A + 2), fa.FA_ERR_ALIGN), (dict(lse=A + 32 * MB + 4), fa.FA_ERR_ALIGN),
+    (dict(o=A), fa.FA_ERR_ALIAS), (dict(lse=A + 24 * MB + 64), fa.FA_ERR_ALIAS),
+    (dict(o=A + 16 * MB + 32), fa.FA_ERR_ALIAS),
+])
+def test_bad_arguments_rejected_on_host(fn, kw, status):
+    assert _call(fn, **kw) == status
+
+
+def test_strerror_covers_every_status():
+    seen = set()
+    for s in range(9):
+        msg = fa.fa_strerror(s)
+        assert msg and msg != "unknown status"
+        seen.add(msg)
+    assert len(seen) == 9
+    assert fa.fa_strerror(12345) == "unknown status"
+
+
+def test_missing_library_fails_loudly(monkeypatch):
+    monkeypatch.setattr(fa.binding, "_lib", None)
+    monkeypatch.setattr(fa.binding, "LIB_PATH", "/nonexistent/libfa_fwd.so")
+    with pytest.raises(ImportError):
+        fa.binding.fa_fwd(A, A, A, A, A, 1, 1, 1, 64, 1.0, 0, None)
