@@ -29,6 +29,9 @@ int validate(const void* q, const void* k, const void* v, const void* o, const f
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED_D;
   const int64_t rows = (int64_t)B * H * N;
   if (rows * d >= kMaxElems) return FA_ERR_SHAPE;
+  // One head's K or V (N x d) must stay below 2 GiB: the kernels address a
+  // head with 32-bit byte offsets.
+  if ((int64_t)N * d * elem_bytes >= (int64_t(1) << 31)) return FA_ERR_SHAPE;
   if (!(scale > 0.f) || !isfinite(scale)) return FA_ERR_SCALE;
   if (causal != 0 && causal != 1) return FA_ERR_CAUSAL;
   if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(o) || misaligned(lse))
@@ -65,7 +68,7 @@ const char* fa_strerror(int status) {
   switch (status) {
     case FA_OK: return "success";
     case FA_ERR_NULL: return "a required pointer is NULL";
-    case FA_ERR_SHAPE: return "B, H and N must be >= 1 and B*H*N*d below 2^40";
+    case FA_ERR_SHAPE: return "B, H, N must be >= 1, B*H*N*d below 2^40 and one head below 2 GiB";
     case FA_ERR_UNSUPPORTED_D: return "head dimension must be 64 or 128";
     case FA_ERR_SCALE: return "scale must be finite and > 0";
     case FA_ERR_ALIGN: return "pointers must be 16-byte aligned";

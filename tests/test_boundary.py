@@ -59,6 +59,7 @@ def _call(fn, **kw):
     (dict(lse=None), fa.FA_ERR_NULL),
     (dict(B=0), fa.FA_ERR_SHAPE), (dict(H=-1), fa.FA_ERR_SHAPE), (dict(N=0), fa.FA_ERR_SHAPE),
     (dict(B=1 << 20, H=1 << 10, N=1 << 10, d=128), fa.FA_ERR_SHAPE),
+    (dict(N=1 << 23, d=128), fa.FA_ERR_SHAPE),
     (dict(d=32), fa.FA_ERR_UNSUPPORTED_D), (dict(d=96), fa.FA_ERR_UNSUPPORTED_D),
     (dict(d=256), fa.FA_ERR_UNSUPPORTED_D),
     (dict(scale=0.0), fa.FA_ERR_SCALE), (dict(scale=-0.5), fa.FA_ERR_SCALE),
