@@ -77,10 +77,13 @@ __device__ __forceinline__ int vt_pos(int k) {
   return (k & ~15) + 8 * ((k >> 2) & 1) + 4 * ((k >> 3) & 1) + (k & 3);
 }
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Two fp32 values -> one word of two bf16 (round to nearest even), one
+// v_cvt_pk_bf16_f32.
 __device__ __forceinline__ unsigned pack_bf16x2(float lo, float hi) {
-  const __bf16 a = (__bf16)lo, b = (__bf16)hi;   // round to nearest even
-  return (unsigned)__builtin_bit_cast(unsigned short, a) |
-         ((unsigned)__builtin_bit_cast(unsigned short, b) << 16);
+  return __builtin_bit_cast(unsigned, __builtin_convertvector((f32x2{lo, hi}), bf16x2));
 }
 
 // max over both halves of the wave: lane l and lane l^32 end with the same value.
@@ -93,208 +96,229 @@ __device__ __forceinline__ float sum_across_halves(float x) {
   return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
 }
 
-// Byte offsets (inside one K tile of the source) that this lane's LDS-DMA
-// loads fetch; a slot in a row's pad position fetches that row's last chunk
-// again (it is never read back).
-template <int D> struct KDma {
-  int voff[Cfg<D>::kDmaPerWave];
-  __device__ KDma(int wave, int lane) {
+// Buffer descriptor over keys [k0, N) of one head's K or V: loads at or past
+// key N are out of range and return zero.
+template <int D>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const unsigned short* head, int k0, int N) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)(head + (int64_t)k0 * D), (short)0,
+                                           (N - k0) * (2 * D), 0x00020000);
+}
+
+template <int D, bool CAUSAL>
+struct Fwd {
+  static constexpr int KS = D / 16, DB = D / 32, KB = kKeys / 32, PS = kKeys / 16;
+  static constexpr int KPT = Cfg<D>::KPT;
+
+  unsigned char* smem;
+  const unsigned short* kh;
+  const unsigned short* vh;
+  int N, wave, l32, hl, qw, qi;
+  float c, thr;
+  bf16x8 qf[KS];          // Q fragments (B operand of S^T = K Q^T)
+  f32x16 acc[DB];         // O^T accumulator: lane holds query l%32
+  float m;                // exponent offset (raw-score units)
+  float l;                // this lane's share of the row sum, relative to m
+  int koff[Cfg<D>::kDmaPerWave];   // source byte offsets of the K LDS-DMA slots
+  int voff[KPT];                   // source byte offsets of the V loads
+  int vt_off;                      // this thread's V^T write offset
+  u32x4 vraw[KPT];                 // V tile in flight (registers)
+
+  __device__ unsigned char* kst(int st) const { return smem + st * Cfg<D>::stage; }
+  __device__ unsigned char* vst(int st) const { return smem + st * Cfg<D>::stage + Cfg<D>::kTile; }
+
+  __device__ void setup_offsets(int tid, int lane) {
+    // K: a wave's LDS-DMA load fills 64 consecutive 16-byte slots of the
+    // padded tile; a slot in a pad position re-fetches the row's last chunk.
 #pragma unroll
     for (int i = 0; i < Cfg<D>::kDmaPerWave; ++i) {
       const int slot = (wave + kWaves * i) * 64 + lane;
       const int r = slot / Cfg<D>::kSlots;
-      const int c = min(slot % Cfg<D>::kSlots, D / 8 - 1);
-      voff[i] = r * (2 * D) + 16 * c;
+      const int cc = min(slot % Cfg<D>::kSlots, D / 8 - 1);
+      koff[i] = r * (2 * D) + 16 * cc;
     }
+    // V: KPT consecutive keys x 8 dims per thread; lanes of a 16-lane group
+    // hold different key groups of the same dims, so their V^T writes fill
+    // one LDS row.
+    const int kg = tid % Cfg<D>::KG, dg = tid / Cfg<D>::KG;
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) voff[i] = (kg * KPT + i) * (2 * D) + 16 * dg;
+    vt_off = 8 * dg * Cfg<D>::vStride + 2 * vt_pos(kg * KPT);
   }
-};
 
-// Queue the K tile starting at key k0 into LDS (asynchronous).  The buffer
-// descriptor spans keys k0..N-1 only, so rows past N read as zero.
-template <int D>
-__device__ __forceinline__ void issue_k(const unsigned short* __restrict__ kh, int k0, int N,
-                                        unsigned char* kst, int wave, const KDma<D>& dma) {
+  // Start loading tile k0: K straight into LDS stage `st`, V into registers.
+  __device__ void issue(int k0, int st) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(kh + (int64_t)k0 * D), (short)0, (N - k0) * (2 * D), 0x00020000);
+    const __amdgpu_buffer_rsrc_t kr = tile_rsrc<D>(kh, k0, N);
+    unsigned char* kdst = kst(st);
 #pragma unroll
-  for (int i = 0; i < Cfg<D>::kDmaPerWave; ++i) {
-    const int blk = wave + kWaves * i;
-    if (Cfg<D>::kDma % kWaves == 0 || blk < Cfg<D>::kDma)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(kst + blk * 1024), 16, dma.voff[i], 0, 0, 0);
-  }
+    for (int i = 0; i < Cfg<D>::kDmaPerWave; ++i) {
+      const int blk = wave + kWaves * i;
+      if (Cfg<D>::kDma % kWaves == 0 || blk < Cfg<D>::kDma)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void*)(kdst + blk * 1024), 16, koff[i], 0, 0, 0);
+    }
+    const __amdgpu_buffer_rsrc_t vr = tile_rsrc<D>(vh, k0, N);
+#pragma unroll
+    for (int i = 0; i < KPT; ++i)
+      vraw[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vr, voff[i], 0, 0));
 #endif
-}
-
-// Load the V tile starting at key k0 into registers (KPT keys x 8 dims).
-template <int D>
-__device__ __forceinline__ void load_v(const unsigned short* __restrict__ vh, int k0, int N, int tid,
-                                       u32x4 (&raw)[Cfg<D>::KPT]) {
-  const int kg = tid % Cfg<D>::KG, dg = tid / Cfg<D>::KG;
-#pragma unroll
-  for (int i = 0; i < Cfg<D>::KPT; ++i) {
-    const int key = k0 + kg * Cfg<D>::KPT + i;
-    raw[i] = u32x4{0u, 0u, 0u, 0u};
-    if (key < N) raw[i] = *reinterpret_cast<const u32x4*>(vh + (int64_t)key * D + 8 * dg);
   }
-}
 
-// Transpose the registers of load_v into a V^T stage.
-template <int D>
-__device__ __forceinline__ void store_vt(unsigned char* vt, int tid, const u32x4 (&raw)[Cfg<D>::KPT]) {
-  constexpr int KPT = Cfg<D>::KPT;
-  const int kg = tid % Cfg<D>::KG, dg = tid / Cfg<D>::KG;
-  unsigned char* base = vt + 8 * dg * Cfg<D>::vStride + 2 * vt_pos(kg * KPT);
+  // Transpose the V registers into V^T stage `st`.
+  __device__ void store_v(int st) {
+    unsigned char* base = vst(st) + vt_off;
 #pragma unroll
-  for (int c2 = 0; c2 < 8; ++c2) {
-    unsigned w[KPT / 2];
+    for (int c2 = 0; c2 < 8; ++c2) {
+      unsigned w[KPT / 2];
 #pragma unroll
-    for (int i = 0; i < KPT; i += 2) {
-      const unsigned a = raw[i][c2 >> 1], b = raw[i + 1][c2 >> 1];
-      w[i / 2] = (c2 & 1) ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
+      for (int i = 0; i < KPT; i += 2) {
+        const unsigned a = vraw[i][c2 >> 1], b = vraw[i + 1][c2 >> 1];
+        w[i / 2] = (c2 & 1) ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
+      }
+      unsigned char* dst = base + c2 * Cfg<D>::vStride;
+      if constexpr (KPT == 4)
+        *reinterpret_cast<u32x2*>(dst) = u32x2{w[0], w[1]};
+      else
+        *reinterpret_cast<unsigned*>(dst) = w[0];
     }
-    unsigned char* dst = base + c2 * Cfg<D>::vStride;
-    if constexpr (KPT == 4)
-      *reinterpret_cast<u32x2*>(dst) = u32x2{w[0], w[1]};
-    else
-      *reinterpret_cast<unsigned*>(dst) = w[0];
   }
-}
 
-// Per-wave state of the online softmax for its 32 query rows.
-template <int D>
-struct RowState {
-  f32x16 acc[D / 32];   // O^T accumulator: lane holds query l%32
-  float m;              // exponent offset (raw-score units), lags the max by < 8/c
-  float l;              // this lane's share of the row sum, relative to m
-};
-
-// Consume one K/V tile from LDS: S^T = K Q^T, softmax merge, O^T += V^T P^T.
-template <int D, bool MASK, bool CAUSAL>
-__device__ __forceinline__ void consume_tile(const unsigned char* kst, const unsigned char* vt,
-                                             const bf16x8 (&qf)[D / 16], RowState<D>& st,
-                                             int k0, int qi, int N, int l32, int hl, float c,
-                                             float thr) {
-  constexpr int KS = D / 16, DB = D / 32, KB = kKeys / 32, PS = kKeys / 16;
-  f32x16 s[KB];
-#pragma unroll
-  for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-      const bf16x8 kf = *reinterpret_cast<const bf16x8*>(
-          kst + (32 * kb + l32) * Cfg<D>::kStride + 32 * ks + 16 * hl);
-      s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], s[kb], 0, 0, 0);
-    }
-
-  if constexpr (MASK) {
+  // Consume one K/V tile from LDS: S^T = K Q^T, softmax merge, O^T += V^T P^T.
+  template <bool MASK>
+  __device__ void consume(int st, int k0) {
+    const unsigned char* kt = kst(st) + l32 * Cfg<D>::kStride + 16 * hl;
+    const unsigned char* vt = vst(st) + l32 * Cfg<D>::vStride + 16 * hl;
+    f32x16 s[KB];
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = k0 + 32 * kb + (r & 3) + 8 * (r >> 2) + 4 * hl;
-        if (key >= N || (CAUSAL && key > qi)) s[kb][r] = -INFINITY;
+      for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kt + 32 * kb * Cfg<D>::kStride + 32 * ks);
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], s[kb], 0, 0, 0);
+      }
+
+    if constexpr (MASK) {
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = k0 + 32 * kb + (r & 3) + 8 * (r >> 2) + 4 * hl;
+          if (key >= N || (CAUSAL && key > qi)) s[kb][r] = -INFINITY;
+        }
+    }
+
+    float mx = s[0][0];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int r = (kb == 0 ? 1 : 0); r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+    mx = max_across_halves(mx);
+    // Move the offset only when this row's max ran more than `thr` past it
+    // (always on the first tile, where m = -inf).
+    const bool upd = mx > m + thr;
+    const float m_new = upd ? mx : m;
+    if (__builtin_amdgcn_ballot_w64(upd)) {
+      asm volatile("" ::: "memory");   // keep this a taken/skipped branch
+      const float alpha = __builtin_amdgcn_exp2f((m - m_new) * c);   // 1 if kept, 0 at start
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
+      l *= alpha;
+      m = m_new;
+    }
+    const float mc = m * c;
+
+    bf16x8 pf[PS];
+    float ps0 = 0.f, ps1 = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        u32x4 w;
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * half + e], c, -mc));
+          const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * half + e + 1], c, -mc));
+          ps0 += p0;
+          ps1 += p1;
+          w[e / 2] = pack_bf16x2(p0, p1);
+        }
+        pf[2 * kb + half] = __builtin_bit_cast(bf16x8, w);
+      }
+    l += ps0 + ps1;
+
+#pragma unroll
+    for (int ps = 0; ps < PS; ++ps)
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const bf16x8 vf = *reinterpret_cast<const bf16x8*>(vt + 32 * db * Cfg<D>::vStride + 32 * ps);
+        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[ps], acc[db], 0, 0, 0);
       }
   }
 
-  float mx = s[0][0];
-#pragma unroll
-  for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-    for (int r = (kb == 0 ? 1 : 0); r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-  mx = max_across_halves(mx);
-  // Move the offset only when this row's max ran more than `thr` past it
-  // (always on the first tile, where m = -inf).
-  const bool upd = mx > st.m + thr;
-  const float m_new = upd ? mx : st.m;
-  const float alpha = __builtin_amdgcn_exp2f((st.m - m_new) * c);   // 1 if kept, 0 at start
-  if (__builtin_amdgcn_ballot_w64(upd)) {
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) st.acc[db][r] *= alpha;
-    st.l *= alpha;
+  // One pipeline step: prefetch tile j+1, consume tile j, land tile j+1.
+  template <bool MASK>
+  __device__ void step(int j, int n_tiles) {
+    const int cur = j & 1;
+    const int k0 = j * kKeys;
+    const bool more = j + 1 < n_tiles;
+    if (more) issue(k0 + kKeys, cur ^ 1);
+    // Causal: a wave whose last query precedes the tile's first key has
+    // nothing to do here; the barrier below stays unconditional.
+    if (!MASK || !CAUSAL || k0 <= qw + 31) consume<MASK>(cur, k0);
+    if (more) store_v(cur ^ 1);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
   }
-  st.m = m_new;
-  const float mc = m_new * c;
-
-  bf16x8 pf[PS];
-  float psum = 0.f;
-#pragma unroll
-  for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      u32x4 w;
-#pragma unroll
-      for (int e = 0; e < 8; e += 2) {
-        const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * half + e], c, -mc));
-        const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * half + e + 1], c, -mc));
-        psum += p0 + p1;
-        w[e / 2] = pack_bf16x2(p0, p1);
-      }
-      pf[2 * kb + half] = __builtin_bit_cast(bf16x8, w);
-    }
-  st.l += psum;
-
-#pragma unroll
-  for (int ps = 0; ps < PS; ++ps)
-#pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      const bf16x8 vf = *reinterpret_cast<const bf16x8*>(
-          vt + (32 * db + l32) * Cfg<D>::vStride + 32 * ps + 16 * hl);
-      st.acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[ps], st.acc[db], 0, 0, 0);
-    }
-}
+};
 
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     const unsigned short* __restrict__ q, const unsigned short* __restrict__ k,
     const unsigned short* __restrict__ v, unsigned short* __restrict__ o,
     float* __restrict__ lse, int N, int BH, int n_qtiles, float scale) {
-  constexpr int KS = D / 16, DB = D / 32;
   __shared__ __attribute__((aligned(1024))) unsigned char smem[Cfg<D>::lds];
-  auto kst = [&](int st) { return smem + st * Cfg<D>::stage; };
-  auto vst = [&](int st) { return smem + st * Cfg<D>::stage + Cfg<D>::kTile; };
+  constexpr int KS = D / 16, DB = D / 32;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int l32 = lane & 31;
-  const int hl = lane >> 5;
-
   // Heaviest query tiles first (causal work grows with the tile index); heads
   // vary fastest, so with B*H a multiple of 8 every tile of a head lands on
   // the same XCD and shares its L2.
   const int bh = blockIdx.x % BH;
   const int qt = n_qtiles - 1 - (int)(blockIdx.x / BH);
   const int q0 = qt * kRows;
-  const int qw = q0 + wave * 32;          // first query row of this wave
-  const int qi = qw + l32;                // this lane's query row
   const int64_t head = (int64_t)bh * N * D;
-  const unsigned short* kh = k + head;
-  const unsigned short* vh = v + head;
-  const float c = scale * kLog2e;
-  const float thr = kLazy / c;
 
-  // Q fragments (B operand of S^T = K Q^T), resident for the whole loop.
-  bf16x8 qf[KS];
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    u32x4 raw = {0u, 0u, 0u, 0u};
-    if (qi < N) raw = *reinterpret_cast<const u32x4*>(q + head + (int64_t)qi * D + 16 * ks + 8 * hl);
-    qf[ks] = __builtin_bit_cast(bf16x8, raw);
-  }
-
-  RowState<D> st;
+  Fwd<D, CAUSAL> f;
+  f.smem = smem;
+  f.kh = k + head;
+  f.vh = v + head;
+  f.N = N;
+  f.wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  f.l32 = lane & 31;
+  f.hl = lane >> 5;
+  f.qw = q0 + f.wave * 32;
+  f.qi = f.qw + f.l32;
+  f.c = scale * kLog2e;
+  f.thr = kLazy / f.c;
+  f.m = -INFINITY;
+  f.l = 0.f;
 #pragma unroll
   for (int db = 0; db < DB; ++db)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) st.acc[db][r] = 0.f;
-  st.m = -INFINITY;
-  st.l = 0.f;
+    for (int r = 0; r < 16; ++r) f.acc[db][r] = 0.f;
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    u32x4 raw = {0u, 0u, 0u, 0u};
+    if (f.qi < N) raw = *reinterpret_cast<const u32x4*>(q + head + (int64_t)f.qi * D + 16 * ks + 8 * f.hl);
+    f.qf[ks] = __builtin_bit_cast(bf16x8, raw);
+  }
+  f.setup_offsets(tid, lane);
 
   const int kv_end = CAUSAL ? min(N, q0 + kRows) : N;
   const int n_tiles = (kv_end + kKeys - 1) / kKeys;
@@ -302,47 +326,29 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
   // precedes the workgroup's first query.
   const int n_full = CAUSAL ? min(q0, N / kKeys * kKeys) / kKeys : N / kKeys;
 
-  const KDma<D> dma(wave, lane);
-  u32x4 vraw[Cfg<D>::KPT];
-  issue_k<D>(kh, 0, N, kst(0), wave, dma);
-  load_v<D>(vh, 0, N, tid, vraw);
-  store_vt<D>(vst(0), tid, vraw);
+  f.issue(0, 0);
+  f.store_v(0);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-
-  for (int j = 0; j < n_tiles; ++j) {
-    const int cur = j & 1;
-    const int k0 = j * kKeys;
-    const bool more = j + 1 < n_tiles;
-    if (more) {
-      issue_k<D>(kh, k0 + kKeys, N, kst(cur ^ 1), wave, dma);
-      load_v<D>(vh, k0 + kKeys, N, tid, vraw);
-    }
-    if (j < n_full) {
-      consume_tile<D, false, CAUSAL>(kst(cur), vst(cur), qf, st, k0, qi, N, l32, hl, c, thr);
-    } else if (!CAUSAL || k0 <= qw + 31) {   // a wave wholly above the diagonal skips the tile
-      consume_tile<D, true, CAUSAL>(kst(cur), vst(cur), qf, st, k0, qi, N, l32, hl, c, thr);
-    }
-    if (more) store_vt<D>(vst(cur ^ 1), tid, vraw);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-  }
+  int j = 0;
+  for (; j < n_full; ++j) f.template step<false>(j, n_tiles);
+  for (; j < n_tiles; ++j) f.template step<true>(j, n_tiles);
 
   // Epilogue: O = acc / l in bf16 (round to nearest even), LSE = scale*m + ln l.
-  const float l_tot = sum_across_halves(st.l);
-  if (qi < N) {
+  const float l_tot = sum_across_halves(f.l);
+  if (f.qi < N) {
     const float inv = 1.f / l_tot;
-    unsigned short* orow = o + head + (int64_t)qi * D;
+    unsigned short* orow = o + head + (int64_t)f.qi * D;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int dim = 32 * db + 8 * g + 4 * hl;
-        const u32x2 w = {pack_bf16x2(st.acc[db][4 * g] * inv, st.acc[db][4 * g + 1] * inv),
-                         pack_bf16x2(st.acc[db][4 * g + 2] * inv, st.acc[db][4 * g + 3] * inv)};
+        const int dim = 32 * db + 8 * g + 4 * f.hl;
+        const u32x2 w = {pack_bf16x2(f.acc[db][4 * g] * inv, f.acc[db][4 * g + 1] * inv),
+                         pack_bf16x2(f.acc[db][4 * g + 2] * inv, f.acc[db][4 * g + 3] * inv)};
         *reinterpret_cast<u32x2*>(orow + dim) = w;
       }
-    if (hl == 0) lse[(int64_t)bh * N + qi] = st.m * scale + logf(l_tot);
+    if (f.hl == 0) lse[(int64_t)bh * N + f.qi] = f.m * scale + logf(l_tot);
   }
 }
 
