@@ -17,14 +17,15 @@
 //     max and row sum are in-lane reductions plus one v_permlane32_swap;
 //   * the output is accumulated transposed as well, O^T += V^T P^T: the
 //     probabilities are used in place as the B operand (rounded to bf16) and
-//     V^T comes from LDS, where V is stored transposed with the keys of each
-//     16-key group permuted into the accumulator's order, so each lane
-//     fetches its 8 keys with one 16-byte LDS read.
-// Pipeline: K/V tiles are double-buffered in LDS.  While tile j is consumed,
-// K of tile j+1 streams straight into LDS (buffer_load_dwordx4 ... lds) and V
-// of tile j+1 into registers, to be transposed into LDS after the products of
-// tile j; one barrier per tile.  LDS rows are padded by 16 bytes so that the
-// fragment reads of 16 consecutive rows hit distinct banks.
+//     V^T is read from row-major V in LDS with ds_read_b64_tr_b16, whose
+//     16-lane transpose hands each lane 4 keys of one head dimension; two
+//     such reads give the 8 keys, in the accumulator's key order, that the
+//     lane's probabilities cover.
+// Pipeline: K/V tiles are double-buffered in LDS and stream straight from
+// memory into LDS (buffer_load_dwordx4 ... lds, range-checked so keys past N
+// read as zero) while the previous tile is consumed; one barrier per tile.
+// LDS rows are padded so that fragment reads hit distinct banks with every
+// lane's addresses a compile-time offset from one base.
 // Rescaling is lazy: the running max used as the exponent's offset only moves
 // when a row's max exceeds it by more than 8/c (c = scale*log2 e), so
 // probabilities stay <= 2^8 and the accumulator is rescaled rarely; since O
@@ -44,6 +45,8 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void lds_void;
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
@@ -53,29 +56,21 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLazy = 8.0f;             // log2 headroom before a rescale
 
 template <int D> struct Cfg {
-  // LDS rows carry one 16-byte pad chunk, so the fragment reads of 16
-  // consecutive rows fall in 16 distinct bank groups while every lane's
-  // fragment addresses stay a compile-time offset from one base.
-  static constexpr int kSlots = D / 8 + 1;          // 16-byte slots per K row
-  static constexpr int kStride = 16 * kSlots;       // bytes per K row
-  static constexpr int vStride = 2 * kKeys + 16;    // bytes per V^T row
-  static constexpr int kTile = kKeys * kStride;     // bytes of one K tile
-  static constexpr int vTile = D * vStride;         // bytes of one V^T tile
+  // K rows carry one 16-byte pad chunk, so the 16-byte fragment reads of 16
+  // consecutive rows fall in distinct bank groups.  V rows are padded so that
+  // the four rows a transposed read touches land in four distinct quarters
+  // of the banks.
+  static constexpr int kStride = 2 * D + 16;           // bytes per K row
+  static constexpr int vStride = D == 128 ? 320 : 192; // bytes per V row
+  static constexpr int kTile = kKeys * kStride;        // bytes of one K tile
+  static constexpr int vTile = kKeys * vStride;        // bytes of one V tile
   static constexpr int stage = kTile + vTile;
-  static constexpr int lds = 2 * stage;             // double-buffered
-  static constexpr int kDma = kTile / 1024;         // 1 KB LDS-DMA loads per K tile
+  static constexpr int lds = 2 * stage;                // double-buffered
+  static constexpr int kDma = kTile / 1024;            // 1 KB LDS-DMA loads per tile
+  static constexpr int vDma = vTile / 1024;
   static constexpr int kDmaPerWave = (kDma + kWaves - 1) / kWaves;
-  static constexpr int DG = D / 8;                  // 8-dim groups of a V row
-  static constexpr int KPT = kKeys * DG / kThreads; // V keys per thread (2, 4)
-  static constexpr int KG = kKeys / KPT;            // key groups
+  static constexpr int vDmaPerWave = (vDma + kWaves - 1) / kWaves;
 };
-
-// Position of key k (0..63) inside a V^T row: in each 16-key group, key
-// (e%4) + 8*(e/4) + 4*h sits at 8*h + e, the order in which the score
-// accumulator hands its keys to the P.V product.
-__device__ __forceinline__ int vt_pos(int k) {
-  return (k & ~15) + 8 * ((k >> 2) & 1) + 4 * ((k >> 3) & 1) + (k & 3);
-}
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -104,10 +99,20 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const unsigned short
                                            (N - k0) * (2 * D), 0x00020000);
 }
 
+// Source byte offset (inside one tile of K or V) fetched by LDS-DMA slot
+// `slot` of a tile whose LDS rows are `stride` bytes long; a slot in a pad
+// position re-fetches the row's last chunk (never read back).
+template <int D>
+__device__ __forceinline__ int dma_offset(int slot, int stride) {
+  const int slots = stride / 16;
+  const int r = slot / slots;
+  const int cc = min(slot % slots, D / 8 - 1);
+  return r * (2 * D) + 16 * cc;
+}
+
 template <int D, bool CAUSAL>
 struct Fwd {
   static constexpr int KS = D / 16, DB = D / 32, KB = kKeys / 32, PS = kKeys / 16;
-  static constexpr int KPT = Cfg<D>::KPT;
 
   unsigned char* smem;
   const unsigned short* kh;
@@ -119,74 +124,53 @@ struct Fwd {
   float m;                // exponent offset (raw-score units)
   float l;                // this lane's share of the row sum, relative to m
   int koff[Cfg<D>::kDmaPerWave];   // source byte offsets of the K LDS-DMA slots
-  int voff[KPT];                   // source byte offsets of the V loads
-  int vt_off;                      // this thread's V^T write offset
-  u32x4 vraw[KPT];                 // V tile in flight (registers)
+  int voff[Cfg<D>::vDmaPerWave];   // source byte offsets of the V LDS-DMA slots
+  int k_rd, v_rd;                  // this lane's fragment read offsets in a stage
 
   __device__ unsigned char* kst(int st) const { return smem + st * Cfg<D>::stage; }
   __device__ unsigned char* vst(int st) const { return smem + st * Cfg<D>::stage + Cfg<D>::kTile; }
 
-  __device__ void setup_offsets(int tid, int lane) {
-    // K: a wave's LDS-DMA load fills 64 consecutive 16-byte slots of the
-    // padded tile; a slot in a pad position re-fetches the row's last chunk.
+  __device__ void setup_offsets(int lane) {
 #pragma unroll
-    for (int i = 0; i < Cfg<D>::kDmaPerWave; ++i) {
-      const int slot = (wave + kWaves * i) * 64 + lane;
-      const int r = slot / Cfg<D>::kSlots;
-      const int cc = min(slot % Cfg<D>::kSlots, D / 8 - 1);
-      koff[i] = r * (2 * D) + 16 * cc;
-    }
-    // V: KPT consecutive keys x 8 dims per thread; lanes of a 16-lane group
-    // hold different key groups of the same dims, so their V^T writes fill
-    // one LDS row.
-    const int kg = tid % Cfg<D>::KG, dg = tid / Cfg<D>::KG;
+    for (int i = 0; i < Cfg<D>::kDmaPerWave; ++i)
+      koff[i] = dma_offset<D>((wave + kWaves * i) * 64 + lane, Cfg<D>::kStride);
 #pragma unroll
-    for (int i = 0; i < KPT; ++i) voff[i] = (kg * KPT + i) * (2 * D) + 16 * dg;
-    vt_off = 8 * dg * Cfg<D>::vStride + 2 * vt_pos(kg * KPT);
+    for (int i = 0; i < Cfg<D>::vDmaPerWave; ++i)
+      voff[i] = dma_offset<D>((wave + kWaves * i) * 64 + lane, Cfg<D>::vStride);
+    k_rd = l32 * Cfg<D>::kStride + 16 * hl;
+    // Transposed V reads: in each 16-lane group g, lane 4e + j addresses key
+    // row 4*(g/2) + e and head dims 16*(g%2) + 4j .. +3 of a 32-dim block.
+    const int g = lane >> 4, e = (lane >> 2) & 3, j = lane & 3;
+    v_rd = (4 * (g >> 1) + e) * Cfg<D>::vStride + 2 * (16 * (g & 1) + 4 * j);
   }
 
-  // Start loading tile k0: K straight into LDS stage `st`, V into registers.
+  // Start streaming the tile at key k0 into LDS stage `st` (asynchronous).
   __device__ void issue(int k0, int st) {
 #if defined(__HIP_DEVICE_COMPILE__)
     const __amdgpu_buffer_rsrc_t kr = tile_rsrc<D>(kh, k0, N);
+    const __amdgpu_buffer_rsrc_t vr = tile_rsrc<D>(vh, k0, N);
     unsigned char* kdst = kst(st);
+    unsigned char* vdst = vst(st);
 #pragma unroll
     for (int i = 0; i < Cfg<D>::kDmaPerWave; ++i) {
       const int blk = wave + kWaves * i;
       if (Cfg<D>::kDma % kWaves == 0 || blk < Cfg<D>::kDma)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void*)(kdst + blk * 1024), 16, koff[i], 0, 0, 0);
     }
-    const __amdgpu_buffer_rsrc_t vr = tile_rsrc<D>(vh, k0, N);
 #pragma unroll
-    for (int i = 0; i < KPT; ++i)
-      vraw[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vr, voff[i], 0, 0));
-#endif
-  }
-
-  // Transpose the V registers into V^T stage `st`.
-  __device__ void store_v(int st) {
-    unsigned char* base = vst(st) + vt_off;
-#pragma unroll
-    for (int c2 = 0; c2 < 8; ++c2) {
-      unsigned w[KPT / 2];
-#pragma unroll
-      for (int i = 0; i < KPT; i += 2) {
-        const unsigned a = vraw[i][c2 >> 1], b = vraw[i + 1][c2 >> 1];
-        w[i / 2] = (c2 & 1) ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
-      }
-      unsigned char* dst = base + c2 * Cfg<D>::vStride;
-      if constexpr (KPT == 4)
-        *reinterpret_cast<u32x2*>(dst) = u32x2{w[0], w[1]};
-      else
-        *reinterpret_cast<unsigned*>(dst) = w[0];
+    for (int i = 0; i < Cfg<D>::vDmaPerWave; ++i) {
+      const int blk = wave + kWaves * i;
+      if (Cfg<D>::vDma % kWaves == 0 || blk < Cfg<D>::vDma)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void*)(vdst + blk * 1024), 16, voff[i], 0, 0, 0);
     }
+#endif
   }
 
   // Consume one K/V tile from LDS: S^T = K Q^T, softmax merge, O^T += V^T P^T.
   template <bool MASK>
   __device__ void consume(int st, int k0) {
-    const unsigned char* kt = kst(st) + l32 * Cfg<D>::kStride + 16 * hl;
-    const unsigned char* vt = vst(st) + l32 * Cfg<D>::vStride + 16 * hl;
+    const unsigned char* kt = kst(st) + k_rd;
+    const unsigned char* vt = vst(st) + v_rd;
     f32x16 s[KB];
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
@@ -232,8 +216,12 @@ struct Fwd {
     }
     const float mc = m * c;
 
+    // Probabilities, rounded to bf16 for the product; the row sum is taken
+    // over the same rounded values (two per v_dot2_f32_bf16), so numerator
+    // and denominator see identical weights.
     bf16x8 pf[PS];
     float ps0 = 0.f, ps1 = 0.f;
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
@@ -243,9 +231,13 @@ struct Fwd {
         for (int e = 0; e < 8; e += 2) {
           const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * half + e], c, -mc));
           const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * half + e + 1], c, -mc));
-          ps0 += p0;
-          ps1 += p1;
-          w[e / 2] = pack_bf16x2(p0, p1);
+          // dot2 of the converted pair itself: taking it from an element of
+          // the vector under construction is miscompiled (the same element
+          // is summed repeatedly).
+          const bf16x2 pb = __builtin_convertvector((f32x2{p0, p1}), bf16x2);
+          if (e & 2) ps1 = __builtin_amdgcn_fdot2_f32_bf16(pb, ones, ps1, false);
+          else       ps0 = __builtin_amdgcn_fdot2_f32_bf16(pb, ones, ps0, false);
+          w[e / 2] = __builtin_bit_cast(unsigned, pb);
         }
         pf[2 * kb + half] = __builtin_bit_cast(bf16x8, w);
       }
@@ -255,7 +247,10 @@ struct Fwd {
     for (int ps = 0; ps < PS; ++ps)
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        const bf16x8 vf = *reinterpret_cast<const bf16x8*>(vt + 32 * db * Cfg<D>::vStride + 32 * ps);
+        const unsigned char* src = vt + 16 * ps * Cfg<D>::vStride + 64 * db;
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)src);
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(src + 8 * Cfg<D>::vStride));
+        const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[ps], acc[db], 0, 0, 0);
       }
   }
@@ -270,7 +265,6 @@ struct Fwd {
     // Causal: a wave whose last query precedes the tile's first key has
     // nothing to do here; the barrier below stays unconditional.
     if (!MASK || !CAUSAL || k0 <= qw + 31) consume<MASK>(cur, k0);
-    if (more) store_v(cur ^ 1);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   }
@@ -318,7 +312,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     if (f.qi < N) raw = *reinterpret_cast<const u32x4*>(q + head + (int64_t)f.qi * D + 16 * ks + 8 * f.hl);
     f.qf[ks] = __builtin_bit_cast(bf16x8, raw);
   }
-  f.setup_offsets(tid, lane);
+  f.setup_offsets(lane);
 
   const int kv_end = CAUSAL ? min(N, q0 + kRows) : N;
   const int n_tiles = (kv_end + kKeys - 1) / kKeys;
@@ -327,7 +321,6 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
   const int n_full = CAUSAL ? min(q0, N / kKeys * kKeys) / kKeys : N / kKeys;
 
   f.issue(0, 0);
-  f.store_v(0);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   int j = 0;
