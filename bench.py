@@ -20,8 +20,14 @@ causal.  Also reported:
 
 --copy-bytes S runs only a plain device-to-device copy of S bytes (used to
 calibrate the FETCH_SIZE / WRITE_SIZE counters) and exits.
+
+--summarize DIR turns the raw rocprofv3 output of one profiling session
+(see PROFILE_STEPS below; no GPU needed) into the text summaries under
+profiles/ that this script and the documentation quote.
 """
 import argparse
+import csv
+import glob
 import hashlib
 import json
 import os
@@ -59,18 +65,21 @@ def measured_traffic(workload_name):
     return t.get("bytes_per_launch")
 
 
-def cpu_baseline(x, w, target_s=12.0):
+def cpu_baseline(x, w, target_s=15.0):
     """Time the fp64 oracle on sampled query rows of the workload."""
     import oracle
     rng = np.random.default_rng(12345)
     total_rows = w.B * w.H * w.N
     n_keys = lambda r: (r % w.N) + 1 if w.causal else w.N   # noqa: E731
-    # calibrate on a small sample, then size the real one to ~target_s
-    rows = np.sort(rng.choice(total_rows, size=64, replace=False)).astype(np.int64)
+    # warm the thread pool, calibrate on a small sample, then size the timed
+    # sample to about target_s seconds
+    warm = np.arange(16, dtype=np.int64)
+    oracle.attention_c(x["q"], x["k"], x["v"], w.scale, w.causal, rows=warm)
+    rows = np.sort(rng.choice(total_rows, size=512, replace=False)).astype(np.int64)
     t0 = time.perf_counter()
     oracle.attention_c(x["q"], x["k"], x["v"], w.scale, w.causal, rows=rows)
     t_cal = time.perf_counter() - t0
-    n = int(min(total_rows, max(64, 64 * target_s / max(t_cal, 1e-6))))
+    n = int(min(total_rows, max(512, 512 * target_s / max(t_cal, 1e-6))))
     rows = np.sort(rng.choice(total_rows, size=n, replace=False)).astype(np.int64)
     t0 = time.perf_counter()
     oracle.attention_c(x["q"], x["k"], x["v"], w.scale, w.causal, rows=rows)
@@ -93,6 +102,109 @@ def copy_calibration(nbytes):
     print(json.dumps({"copy_bytes": nbytes, "launches": 5}))
 
 
+# The profiling session whose output --summarize reads.  Each step is run on
+# the GPU host from the repository root with OUT set to an output folder.
+PROFILE_STEPS = {
+    "trace": "rocprofv3 --kernel-trace --stats --output-format csv -d $OUT/trace -o run "
+             "-- python bench.py --steps 20 --warmup 3 --no-cpu-baseline",
+    "fetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d $OUT/fetch -o run "
+             "-- python bench.py --steps 3 --warmup 1 --no-cpu-baseline",
+    "write": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d $OUT/write -o run "
+             "-- python bench.py --steps 3 --warmup 1 --no-cpu-baseline",
+    "copy_fetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d $OUT/copy_fetch -o run "
+                  "-- python bench.py --copy-bytes 268435456",
+    "copy_write": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d $OUT/copy_write -o run "
+                  "-- python bench.py --copy-bytes 268435456",
+    "sq": "rocprofv3 --pmc SQ_WAVE_CYCLES SQ_BUSY_CYCLES SQ_VALU_MFMA_BUSY_CYCLES "
+          "SQ_VALU_MFMA_COEXEC_CYCLES SQ_ACTIVE_INST_VALU SQ_WAIT_INST_LDS SQ_WAIT_ANY "
+          "SQ_LDS_BANK_CONFLICT GRBM_GUI_ACTIVE --output-format csv -d $OUT/sq -o run "
+          "-- python bench.py --steps 3 --warmup 1 --no-cpu-baseline",
+    "sq2": "rocprofv3 --pmc SQ_INSTS_VALU SQ_INSTS_MFMA SQ_INSTS_LDS SQ_INSTS_SALU "
+           "SQ_ACTIVE_INST_LDS SQ_INSTS_VALU_TRANS_F32 SQ_ACTIVE_INST_ANY GRBM_GUI_ACTIVE "
+           "--output-format csv -d $OUT/sq2 -o run "
+           "-- python bench.py --steps 3 --warmup 1 --no-cpu-baseline",
+}
+KERNEL_KEY = "fwd_bf16_kernel"
+COPY_KEY = "copy"
+
+
+def _counters(folder, key):
+    """{counter: [per-dispatch totals]} for kernels whose name contains key."""
+    per = {}
+    for f in glob.glob(os.path.join(folder, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            for row in csv.DictReader(fh):
+                if key not in row["Kernel_Name"]:
+                    continue
+                d = per.setdefault(row["Counter_Name"], {})
+                d[row["Dispatch_Id"]] = d.get(row["Dispatch_Id"], 0.0) + float(row["Counter_Value"])
+    return {k: list(v.values()) for k, v in per.items()}
+
+
+def summarize(out_dir, workload_name):
+    prof = os.path.join(ROOT, "profiles")
+    os.makedirs(prof, exist_ok=True)
+    src_hash = kernel_source_hash()
+    lines = []
+    # kernel trace
+    stats = glob.glob(os.path.join(out_dir, "trace", "**", "*kernel_stats.csv"), recursive=True)
+    avg_ns = None
+    with open(stats[0]) as fh:
+        for row in csv.DictReader(fh):
+            if KERNEL_KEY in row["Name"]:
+                avg_ns = float(row["AverageNs"])
+                lines.append("kernel: %s" % row["Name"])
+                lines.append("calls=%s  average=%.1f us  min=%.1f us  max=%.1f us" % (
+                    row["Calls"], float(row["AverageNs"]) / 1e3, float(row["MinNs"]) / 1e3,
+                    float(row["MaxNs"]) / 1e3))
+    with open(os.path.join(prof, "fa_fwd_bf16_%s_kernel_trace.txt" % workload_name), "w") as f:
+        f.write("# rocprofv3 kernel trace, workload %s (kernel source %s)\n" % (workload_name, src_hash))
+        f.write("# command: %s\n" % PROFILE_STEPS["trace"])
+        f.write("\n".join(lines) + "\n")
+    # HBM traffic, calibrated on a copy of known size
+    fetch = _counters(os.path.join(out_dir, "fetch"), KERNEL_KEY)["FETCH_SIZE"]
+    write = _counters(os.path.join(out_dir, "write"), KERNEL_KEY)["WRITE_SIZE"]
+    cf = _counters(os.path.join(out_dir, "copy_fetch"), COPY_KEY)["FETCH_SIZE"]
+    cw = _counters(os.path.join(out_dir, "copy_write"), COPY_KEY)["WRITE_SIZE"]
+    copy_bytes = 268435456
+    f_fetch = copy_bytes / (np.mean(cf) * 1024)
+    f_write = copy_bytes / (np.mean(cw) * 1024)
+    rd = float(np.mean(fetch)) * 1024 * f_fetch
+    wr = float(np.mean(write)) * 1024 * f_write
+    traffic = {"workload": workload_name, "source_hash": src_hash,
+               "fetch_kib_per_launch": float(np.mean(fetch)), "write_kib_per_launch": float(np.mean(write)),
+               "copy_calibration": {"bytes": copy_bytes, "fetch_kib": float(np.mean(cf)),
+                                    "write_kib": float(np.mean(cw)), "fetch_factor": f_fetch,
+                                    "write_factor": f_write},
+               "read_bytes_per_launch": rd, "write_bytes_per_launch": wr,
+               "bytes_per_launch": rd + wr,
+               "commands": [PROFILE_STEPS[k] for k in ("fetch", "write", "copy_fetch", "copy_write")]}
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(traffic, f, indent=1)
+    # SQ counters
+    sq_lines = []
+    sq = {}
+    for part in ("sq", "sq2"):
+        if os.path.isdir(os.path.join(out_dir, part)):
+            for k, v in _counters(os.path.join(out_dir, part), KERNEL_KEY).items():
+                sq[k] = float(np.mean(v))
+    if sq:
+        gui = sq.get("GRBM_GUI_ACTIVE", 0.0) / 8.0          # summed over 8 XCDs
+        for k in sorted(sq):
+            sq_lines.append("%-28s %.4g" % (k, sq[k]))
+        if gui:
+            sq_lines.append("derived: MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE/XCD * 1024 SIMDs) = %.1f %%"
+                            % (100 * sq.get("SQ_VALU_MFMA_BUSY_CYCLES", 0) / (gui * 1024)))
+            sq_lines.append("derived: VALU+MFMA co-issue = SQ_VALU_MFMA_COEXEC_CYCLES / (GRBM_GUI_ACTIVE/XCD * 1024) = %.1f %%"
+                            % (100 * sq.get("SQ_VALU_MFMA_COEXEC_CYCLES", 0) / (gui * 1024)))
+        with open(os.path.join(prof, "fa_fwd_bf16_%s_counters.txt" % workload_name), "w") as f:
+            f.write("# rocprofv3 counters per launch, workload %s (kernel source %s)\n" % (workload_name, src_hash))
+            f.write("# commands:\n#   %s\n#   %s\n" % (PROFILE_STEPS["sq"], PROFILE_STEPS["sq2"]))
+            f.write("\n".join(sq_lines) + "\n")
+    print(json.dumps({"kernel_avg_us": avg_ns / 1e3 if avg_ns else None,
+                      "traffic_bytes": rd + wr, "read": rd, "write": wr}))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -101,7 +213,13 @@ def main():
     ap.add_argument("--workload", type=int, default=4, help="workload id 1..5")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-bytes", type=int, default=0)
+    ap.add_argument("--summarize", metavar="DIR", default=None)
     args = ap.parse_args()
+
+    if args.summarize:
+        from io_aware_softmax_fwd_amd import workloads as W
+        summarize(args.summarize, W.WORKLOADS[args.workload].name)
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on one GPU only; the forward pass shards by "
