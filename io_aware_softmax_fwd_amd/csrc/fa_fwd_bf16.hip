@@ -21,9 +21,12 @@
 //     16-lane transpose hands each lane 4 keys of one head dimension; two
 //     such reads give the 8 keys, in the accumulator's key order, that the
 //     lane's probabilities cover.
-// Pipeline: K/V tiles are double-buffered in LDS and stream straight from
-// memory into LDS (buffer_load_dwordx4 ... lds, range-checked so keys past N
-// read as zero) while the previous tile is consumed; one barrier per tile.
+// Pipeline: K and V tiles stream straight from memory into LDS
+// (buffer_load_dwordx4 ... lds, range-checked so keys past N read as zero),
+// one tile ahead, double-buffered in four separate LDS arrays picked at
+// compile time (the tile loop is unrolled by two); one barrier per tile.
+// Separate arrays let the compiler see that the in-flight loads never touch
+// the buffers being read, so the loads get the whole step to land.
 // LDS rows are padded so that fragment reads hit distinct banks with every
 // lane's addresses a compile-time offset from one base.
 // Rescaling is lazy: the running max used as the exponent's offset only moves
@@ -50,7 +53,6 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kRows = 32 * kWaves;        // query rows per workgroup (Br)
 constexpr int kKeys = 64;                 // keys per K/V tile (Bc)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLazy = 8.0f;             // log2 headroom before a rescale
@@ -64,8 +66,7 @@ template <int D> struct Cfg {
   static constexpr int vStride = D == 128 ? 320 : 192; // bytes per V row
   static constexpr int kTile = kKeys * kStride;        // bytes of one K tile
   static constexpr int vTile = kKeys * vStride;        // bytes of one V tile
-  static constexpr int stage = kTile + vTile;
-  static constexpr int lds = 2 * stage;                // double-buffered
+  static constexpr int lds = 2 * (kTile + vTile);      // two K and two V buffers
   static constexpr int kDma = kTile / 1024;            // 1 KB LDS-DMA loads per tile
   static constexpr int vDma = vTile / 1024;
   static constexpr int kDmaPerWave = (kDma + kWaves - 1) / kWaves;
@@ -110,25 +111,29 @@ __device__ __forceinline__ int dma_offset(int slot, int stride) {
   return r * (2 * D) + 16 * cc;
 }
 
-template <int D, bool CAUSAL>
+template <int D, int QB, bool CAUSAL>
 struct Fwd {
   static constexpr int KS = D / 16, DB = D / 32, KB = kKeys / 32, PS = kKeys / 16;
+  static constexpr int WR = 32 * QB;        // query rows per wave
 
-  unsigned char* smem;
   const unsigned short* kh;
   const unsigned short* vh;
-  int N, wave, l32, hl, qw, qi;
+  int N, wave, l32, hl, qw;
   float c, thr;
-  bf16x8 qf[KS];          // Q fragments (B operand of S^T = K Q^T)
-  f32x16 acc[DB];         // O^T accumulator: lane holds query l%32
-  float m;                // exponent offset (raw-score units)
-  float l;                // this lane's share of the row sum, relative to m
+  bf16x8 qf[QB][KS];      // Q fragments (B operand of S^T = K Q^T), per 32-row block
+  f32x16 acc[QB][DB];     // O^T accumulators: lane holds query l%32 of each block
+  float m[QB];            // exponent offsets (raw-score units)
+  float l[QB];            // this lane's share of the row sums, relative to m
   int koff[Cfg<D>::kDmaPerWave];   // source byte offsets of the K LDS-DMA slots
   int voff[Cfg<D>::vDmaPerWave];   // source byte offsets of the V LDS-DMA slots
-  int k_rd, v_rd;                  // this lane's fragment read offsets in a stage
+  int k_rd, v_rd;                  // this lane's fragment read offsets in a buffer
+  // LDS: K and V of two tiles, as four separate arrays selected at compile
+  // time, so the compiler sees that the LDS-DMA writes into one buffer do not
+  // touch the buffers being read and inserts no wait for them.
+  unsigned char* kbuf[2];
+  unsigned char* vbuf[2];
 
-  __device__ unsigned char* kst(int st) const { return smem + st * Cfg<D>::stage; }
-  __device__ unsigned char* vst(int st) const { return smem + st * Cfg<D>::stage + Cfg<D>::kTile; }
+  __device__ int qi(int qb) const { return qw + 32 * qb + l32; }
 
   __device__ void setup_offsets(int lane) {
 #pragma unroll
@@ -144,56 +149,39 @@ struct Fwd {
     v_rd = (4 * (g >> 1) + e) * Cfg<D>::vStride + 2 * (16 * (g & 1) + 4 * j);
   }
 
-  // Start streaming the tile at key k0 into LDS stage `st` (asynchronous).
-  __device__ void issue(int k0, int st) {
+  // Queue this wave's share of K (or V) of the tile at key k0 into LDS
+  // buffer B (asynchronous; completion is awaited with vmcnt).
+  template <bool IS_V, int B>
+  __device__ void issue(int k0) {
 #if defined(__HIP_DEVICE_COMPILE__)
-    const __amdgpu_buffer_rsrc_t kr = tile_rsrc<D>(kh, k0, N);
-    const __amdgpu_buffer_rsrc_t vr = tile_rsrc<D>(vh, k0, N);
-    unsigned char* kdst = kst(st);
-    unsigned char* vdst = vst(st);
+    constexpr int nblk = IS_V ? Cfg<D>::vDma : Cfg<D>::kDma;
+    constexpr int per_wave = IS_V ? Cfg<D>::vDmaPerWave : Cfg<D>::kDmaPerWave;
+    const __amdgpu_buffer_rsrc_t r = tile_rsrc<D>(IS_V ? vh : kh, k0, N);
+    unsigned char* dst = IS_V ? vbuf[B] : kbuf[B];
 #pragma unroll
-    for (int i = 0; i < Cfg<D>::kDmaPerWave; ++i) {
+    for (int i = 0; i < per_wave; ++i) {
       const int blk = wave + kWaves * i;
-      if (Cfg<D>::kDma % kWaves == 0 || blk < Cfg<D>::kDma)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void*)(kdst + blk * 1024), 16, koff[i], 0, 0, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < Cfg<D>::vDmaPerWave; ++i) {
-      const int blk = wave + kWaves * i;
-      if (Cfg<D>::vDma % kWaves == 0 || blk < Cfg<D>::vDma)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void*)(vdst + blk * 1024), 16, voff[i], 0, 0, 0);
+      if (nblk % kWaves == 0 || blk < nblk)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(dst + blk * 1024), 16,
+                                                 IS_V ? voff[i] : koff[i], 0, 0, 0);
     }
 #endif
   }
 
-  // Consume one K/V tile from LDS: S^T = K Q^T, softmax merge, O^T += V^T P^T.
+  // Online-softmax step of one 32-row block for the tile at key k0: moves
+  // the offset when needed (rescaling its accumulator), writes the bf16
+  // probabilities and adds their row sum.
   template <bool MASK>
-  __device__ void consume(int st, int k0) {
-    const unsigned char* kt = kst(st) + k_rd;
-    const unsigned char* vt = vst(st) + v_rd;
-    f32x16 s[KB];
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kt + 32 * kb * Cfg<D>::kStride + 32 * ks);
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], s[kb], 0, 0, 0);
-      }
-
+  __device__ void softmax(int qb, f32x16 (&s)[KB], bf16x8 (&pf)[PS], int k0) {
     if constexpr (MASK) {
+      // key = k0 + 32*kb + (r&3) + 8*(r>>2) + 4*hl must be <= min(qi, N-1)
+      const int lim = (CAUSAL ? min(qi(qb), N - 1) : N - 1) - k0 - 4 * hl;
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = k0 + 32 * kb + (r & 3) + 8 * (r >> 2) + 4 * hl;
-          if (key >= N || (CAUSAL && key > qi)) s[kb][r] = -INFINITY;
-        }
+        for (int r = 0; r < 16; ++r)
+          if (32 * kb + (r & 3) + 8 * (r >> 2) > lim) s[kb][r] = -INFINITY;
     }
-
     float mx = s[0][0];
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
@@ -202,24 +190,22 @@ struct Fwd {
     mx = max_across_halves(mx);
     // Move the offset only when this row's max ran more than `thr` past it
     // (always on the first tile, where m = -inf).
-    const bool upd = mx > m + thr;
-    const float m_new = upd ? mx : m;
+    const bool upd = mx > m[qb] + thr;
     if (__builtin_amdgcn_ballot_w64(upd)) {
       asm volatile("" ::: "memory");   // keep this a taken/skipped branch
-      const float alpha = __builtin_amdgcn_exp2f((m - m_new) * c);   // 1 if kept, 0 at start
+      const float m_new = upd ? mx : m[qb];
+      const float alpha = __builtin_amdgcn_exp2f((m[qb] - m_new) * c);   // 1 if kept, 0 at start
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
-      l *= alpha;
-      m = m_new;
+        for (int r = 0; r < 16; ++r) acc[qb][db][r] *= alpha;
+      l[qb] *= alpha;
+      m[qb] = m_new;
     }
-    const float mc = m * c;
-
+    const float mc = m[qb] * c;
     // Probabilities, rounded to bf16 for the product; the row sum is taken
     // over the same rounded values (two per v_dot2_f32_bf16), so numerator
     // and denominator see identical weights.
-    bf16x8 pf[PS];
     float ps0 = 0.f, ps1 = 0.f;
     const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
@@ -241,7 +227,36 @@ struct Fwd {
         }
         pf[2 * kb + half] = __builtin_bit_cast(bf16x8, w);
       }
-    l += ps0 + ps1;
+    l[qb] += ps0 + ps1;
+  }
+
+  // Consume the tile in buffers PAR: S^T = K Q^T for every block (each K
+  // fragment feeds all blocks), the softmax merges, then O^T += V^T P^T
+  // (each V fragment feeds all blocks).
+  template <bool MASK, int PAR>
+  __device__ void consume(int k0) {
+    const unsigned char* kt = kbuf[PAR] + k_rd;
+    const unsigned char* vt = vbuf[PAR] + v_rd;
+    f32x16 s[QB][KB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[qb][kb][r] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kt + 32 * kb * Cfg<D>::kStride + 32 * ks);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+          s[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[qb][ks], s[qb][kb], 0, 0, 0);
+      }
+
+    bf16x8 pf[QB][PS];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) softmax<MASK>(qb, s[qb], pf[qb], k0);
 
 #pragma unroll
     for (int ps = 0; ps < PS; ++ps)
@@ -251,32 +266,42 @@ struct Fwd {
         const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)src);
         const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(src + 8 * Cfg<D>::vStride));
         const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[ps], acc[db], 0, 0, 0);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+          acc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[qb][ps], acc[qb][db], 0, 0, 0);
       }
   }
 
-  // One pipeline step: prefetch tile j+1, consume tile j, land tile j+1.
-  template <bool MASK>
+  // One pipeline step: queue tile j+1 into the other buffers (it gets the
+  // whole step to land), consume tile j, wait and synchronise.
+  // PAR = j & 1 selects the buffers at compile time.
+  template <bool MASK, int PAR>
   __device__ void step(int j, int n_tiles) {
-    const int cur = j & 1;
     const int k0 = j * kKeys;
-    const bool more = j + 1 < n_tiles;
-    if (more) issue(k0 + kKeys, cur ^ 1);
+    if (j + 1 < n_tiles) {
+      issue<false, PAR ^ 1>(k0 + kKeys);
+      issue<true, PAR ^ 1>(k0 + kKeys);
+    }
     // Causal: a wave whose last query precedes the tile's first key has
-    // nothing to do here; the barrier below stays unconditional.
-    if (!MASK || !CAUSAL || k0 <= qw + 31) consume<MASK>(cur, k0);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
+    // nothing to do here or later; the barrier below stays unconditional.
+    if (!MASK || !CAUSAL || k0 <= qw + WR - 1) consume<MASK, PAR>(k0);
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
   }
 };
 
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
+template <int D, int QB, bool CAUSAL>
+__global__ __launch_bounds__(kThreads, QB == 1 ? 2 : 1) void fwd_bf16_kernel(
     const unsigned short* __restrict__ q, const unsigned short* __restrict__ k,
     const unsigned short* __restrict__ v, unsigned short* __restrict__ o,
     float* __restrict__ lse, int N, int BH, int n_qtiles, float scale) {
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[Cfg<D>::lds];
+  __shared__ __attribute__((aligned(1024))) unsigned char k_lds0[Cfg<D>::kTile];
+  __shared__ __attribute__((aligned(1024))) unsigned char k_lds1[Cfg<D>::kTile];
+  __shared__ __attribute__((aligned(1024))) unsigned char v_lds0[Cfg<D>::vTile];
+  __shared__ __attribute__((aligned(1024))) unsigned char v_lds1[Cfg<D>::vTile];
   constexpr int KS = D / 16, DB = D / 32;
+  constexpr int BR = 32 * QB * kWaves;   // query rows per workgroup
+  using F = Fwd<D, QB, CAUSAL>;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -285,72 +310,91 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
   // the same XCD and shares its L2.
   const int bh = blockIdx.x % BH;
   const int qt = n_qtiles - 1 - (int)(blockIdx.x / BH);
-  const int q0 = qt * kRows;
+  const int q0 = qt * BR;
   const int64_t head = (int64_t)bh * N * D;
 
-  Fwd<D, CAUSAL> f;
-  f.smem = smem;
+  F f;
+  f.kbuf[0] = k_lds0;
+  f.kbuf[1] = k_lds1;
+  f.vbuf[0] = v_lds0;
+  f.vbuf[1] = v_lds1;
   f.kh = k + head;
   f.vh = v + head;
   f.N = N;
   f.wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   f.l32 = lane & 31;
   f.hl = lane >> 5;
-  f.qw = q0 + f.wave * 32;
-  f.qi = f.qw + f.l32;
+  f.qw = q0 + f.wave * F::WR;
   f.c = scale * kLog2e;
   f.thr = kLazy / f.c;
-  f.m = -INFINITY;
-  f.l = 0.f;
 #pragma unroll
-  for (int db = 0; db < DB; ++db)
+  for (int qb = 0; qb < QB; ++qb) {
+    f.m[qb] = -INFINITY;
+    f.l[qb] = 0.f;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) f.acc[db][r] = 0.f;
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    u32x4 raw = {0u, 0u, 0u, 0u};
-    if (f.qi < N) raw = *reinterpret_cast<const u32x4*>(q + head + (int64_t)f.qi * D + 16 * ks + 8 * f.hl);
-    f.qf[ks] = __builtin_bit_cast(bf16x8, raw);
+      for (int r = 0; r < 16; ++r) f.acc[qb][db][r] = 0.f;
+    const int qi = f.qi(qb);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      u32x4 raw = {0u, 0u, 0u, 0u};
+      if (qi < N) raw = *reinterpret_cast<const u32x4*>(q + head + (int64_t)qi * D + 16 * ks + 8 * f.hl);
+      f.qf[qb][ks] = __builtin_bit_cast(bf16x8, raw);
+    }
   }
   f.setup_offsets(lane);
 
-  const int kv_end = CAUSAL ? min(N, q0 + kRows) : N;
+  const int kv_end = CAUSAL ? min(N, q0 + BR) : N;
   const int n_tiles = (kv_end + kKeys - 1) / kKeys;
   // Tiles before n_full need no mask: every key is < N and, when causal,
   // precedes the workgroup's first query.
   const int n_full = CAUSAL ? min(q0, N / kKeys * kKeys) / kKeys : N / kKeys;
 
-  f.issue(0, 0);
+  f.template issue<false, 0>(0);
+  f.template issue<true, 0>(0);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   int j = 0;
-  for (; j < n_full; ++j) f.template step<false>(j, n_tiles);
-  for (; j < n_tiles; ++j) f.template step<true>(j, n_tiles);
+  for (; j + 1 < n_full; j += 2) {
+    f.template step<false, 0>(j, n_tiles);
+    f.template step<false, 1>(j + 1, n_tiles);
+  }
+  if (j < n_full) f.template step<false, 0>(j++, n_tiles);
+  for (; j < n_tiles; ++j) {
+    if (j & 1) f.template step<true, 1>(j, n_tiles);
+    else       f.template step<true, 0>(j, n_tiles);
+  }
 
   // Epilogue: O = acc / l in bf16 (round to nearest even), LSE = scale*m + ln l.
-  const float l_tot = sum_across_halves(f.l);
-  if (f.qi < N) {
-    const float inv = 1.f / l_tot;
-    unsigned short* orow = o + head + (int64_t)f.qi * D;
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+  for (int qb = 0; qb < QB; ++qb) {
+    const float l_tot = sum_across_halves(f.l[qb]);
+    const int qi = f.qi(qb);
+    if (qi < N) {
+      const float inv = 1.f / l_tot;
+      unsigned short* orow = o + head + (int64_t)qi * D;
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int dim = 32 * db + 8 * g + 4 * f.hl;
-        const u32x2 w = {pack_bf16x2(f.acc[db][4 * g] * inv, f.acc[db][4 * g + 1] * inv),
-                         pack_bf16x2(f.acc[db][4 * g + 2] * inv, f.acc[db][4 * g + 3] * inv)};
-        *reinterpret_cast<u32x2*>(orow + dim) = w;
-      }
-    if (f.hl == 0) lse[(int64_t)bh * N + f.qi] = f.m * scale + logf(l_tot);
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int dim = 32 * db + 8 * g + 4 * f.hl;
+          const u32x2 w = {pack_bf16x2(f.acc[qb][db][4 * g] * inv, f.acc[qb][db][4 * g + 1] * inv),
+                           pack_bf16x2(f.acc[qb][db][4 * g + 2] * inv, f.acc[qb][db][4 * g + 3] * inv)};
+          *reinterpret_cast<u32x2*>(orow + dim) = w;
+        }
+      if (f.hl == 0) lse[(int64_t)bh * N + qi] = f.m[qb] * scale + logf(l_tot);
+    }
   }
 }
 
-template <int D, bool CAUSAL>
+template <int D, int QB, bool CAUSAL>
 hipError_t launch(const Problem& p, hipStream_t stream) {
-  const int n_qtiles = (p.N + kRows - 1) / kRows;
+  constexpr int BR = 32 * QB * kWaves;
+  const int n_qtiles = (p.N + BR - 1) / BR;
   const int BH = p.B * p.H;
   const dim3 grid((unsigned)((int64_t)n_qtiles * BH)), block(kThreads);
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL>), grid, block, 0, stream,
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, QB, CAUSAL>), grid, block, 0, stream,
                      static_cast<const unsigned short*>(p.q), static_cast<const unsigned short*>(p.k),
                      static_cast<const unsigned short*>(p.v), static_cast<unsigned short*>(p.o),
                      p.lse, p.N, BH, n_qtiles, p.scale);
@@ -359,9 +403,17 @@ hipError_t launch(const Problem& p, hipStream_t stream) {
 
 }  // namespace
 
+#ifndef FA_QB128
+#define FA_QB128 1
+#endif
+#ifndef FA_QB64
+#define FA_QB64 1
+#endif
+
 hipError_t launch_fwd_bf16(const Problem& p, hipStream_t stream) {
-  if (p.d == 64) return p.causal ? launch<64, true>(p, stream) : launch<64, false>(p, stream);
-  return p.causal ? launch<128, true>(p, stream) : launch<128, false>(p, stream);
+  if (p.d == 64)
+    return p.causal ? launch<64, FA_QB64, true>(p, stream) : launch<64, FA_QB64, false>(p, stream);
+  return p.causal ? launch<128, FA_QB128, true>(p, stream) : launch<128, FA_QB128, false>(p, stream);
 }
 
 }  // namespace fa
