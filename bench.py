@@ -106,7 +106,7 @@ def copy_calibration(nbytes):
 # the GPU host from the repository root with OUT set to an output folder.
 PROFILE_STEPS = {
     "trace": "rocprofv3 --kernel-trace --stats --output-format csv -d $OUT/trace -o run "
-             "-- python bench.py --steps 20 --warmup 3 --no-cpu-baseline",
+             "-- python bench.py --no-cpu-baseline",
     "fetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d $OUT/fetch -o run "
              "-- python bench.py --steps 3 --warmup 1 --no-cpu-baseline",
     "write": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d $OUT/write -o run "
