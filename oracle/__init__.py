@@ -4,9 +4,12 @@ TEST INFRASTRUCTURE.  Only the tests, the smoke check and the benchmark's
 CPU-baseline leg may import this package.  It shares no code with the GPU
 library (io_aware_softmax_fwd_amd): neither imports the other.
 
-What it computes, for every (b, h, i) with Q, K, V of layout [B, H, N, d]:
+What it computes, for every (b, h, i) with Q of layout [B, H, Nq, d] and
+K, V of layout [B, H, Nk, d] (Nq == Nk == N for the square problem):
 
-    s_j   = scale * <q_i, k_j>          j in J_i = {0..N-1}, or {0..i} if causal
+    s_j   = scale * <q_i, k_j>          j in J_i = {0..Nk-1}, or, if causal,
+                                        {0..i + Nk - Nq} (the last query lines
+                                        up with the last key; needs Nq <= Nk)
     m     = max_j s_j
     l     = sum_j exp(s_j - m)
     O_i   = sum_j exp(s_j - m) v_j / l
@@ -51,7 +54,7 @@ def _load():
         lib.oracle_attn_f64.restype = ctypes.c_int
         lib.oracle_attn_f64.argtypes = [
             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
-            ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+            ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
             ctypes.c_double, ctypes.c_int, ctypes.c_void_p, ctypes.c_int64,
             ctypes.c_void_p, ctypes.c_void_p]
         lib.oracle_max_threads.restype = ctypes.c_int
@@ -73,18 +76,21 @@ def _as_f32(x):
 
 
 def attention_c(q, k, v, scale, causal, rows=None):
-    """fp64 attention of float32 inputs [B,H,N,d].
+    """fp64 attention of float32 inputs: q [B,H,Nq,d], k and v [B,H,Nk,d].
 
-    rows: optional 1-D array of flat row indices r = (b*H + h)*N + i.
-    Returns (O, LSE) as float64: O [B,H,N,d] and LSE [B,H,N] when rows is
+    rows: optional 1-D array of flat query-row indices r = (b*H + h)*Nq + i.
+    Returns (O, LSE) as float64: O [B,H,Nq,d] and LSE [B,H,Nq] when rows is
     None, else O [len(rows), d] and LSE [len(rows)].
     """
     q, k, v = _as_f32(q), _as_f32(k), _as_f32(v)
-    if not (q.shape == k.shape == v.shape):
-        raise ValueError("q, k, v must share one shape")
-    B, H, N, d = q.shape
+    if k.shape != v.shape or q.shape[:2] != k.shape[:2] or q.shape[3] != k.shape[3]:
+        raise ValueError("q [B,H,Nq,d], k and v [B,H,Nk,d] expected")
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    if causal and Nq > Nk:
+        raise ValueError("causal attention needs Nq <= Nk")
     if rows is None:
-        nrows = B * H * N
+        nrows = B * H * Nq
         rows_arr = None
     else:
         rows_arr = np.ascontiguousarray(rows, dtype=np.int64).ravel()
@@ -92,14 +98,14 @@ def attention_c(q, k, v, scale, causal, rows=None):
     O = np.empty((nrows, d), dtype=np.float64)
     LSE = np.empty((nrows,), dtype=np.float64)
     rc = _load().oracle_attn_f64(
-        q.ctypes.data, k.ctypes.data, v.ctypes.data, B, H, N, d,
+        q.ctypes.data, k.ctypes.data, v.ctypes.data, B, H, Nq, Nk, d,
         float(scale), int(bool(causal)),
         None if rows_arr is None else rows_arr.ctypes.data, nrows,
         O.ctypes.data, LSE.ctypes.data)
     if rc != 0:
         raise RuntimeError("oracle_attn_f64 failed with code %d" % rc)
     if rows is None:
-        return O.reshape(B, H, N, d), LSE.reshape(B, H, N)
+        return O.reshape(B, H, Nq, d), LSE.reshape(B, H, Nq)
     return O, LSE
 
 
@@ -111,16 +117,19 @@ def attention_np(q, k, v, scale, causal, block_rows=1024):
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
-    B, H, N, d = q.shape
-    O = np.empty((B, H, N, d))
-    LSE = np.empty((B, H, N))
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    if causal and Nq > Nk:
+        raise ValueError("causal attention needs Nq <= Nk")
+    O = np.empty((B, H, Nq, d))
+    LSE = np.empty((B, H, Nq))
     for b in range(B):
         for h in range(H):
-            for r0 in range(0, N, block_rows):
-                r1 = min(N, r0 + block_rows)
-                s = float(scale) * (q[b, h, r0:r1] @ k[b, h].T)   # [rows, N]
+            for r0 in range(0, Nq, block_rows):
+                r1 = min(Nq, r0 + block_rows)
+                s = float(scale) * (q[b, h, r0:r1] @ k[b, h].T)   # [rows, Nk]
                 if causal:
-                    keep = np.arange(N)[None, :] <= np.arange(r0, r1)[:, None]
+                    keep = np.arange(Nk)[None, :] <= (np.arange(r0, r1) + (Nk - Nq))[:, None]
                     s = np.where(keep, s, -np.inf)
                 m = s.max(axis=1, keepdims=True)
                 p = np.exp(s - m)

@@ -14,8 +14,10 @@
  *
  * Readings of what the pages leave open:
  *   - S is scaled by `scale` before the softmax (the pages' demo omits it).
- *   - causal: key j takes part in row i iff j <= i (square problem); a masked
- *     key is excluded outright.
+ *   - causal: key j takes part in query row i iff j <= i + (Nk - Nq), i.e.
+ *     the last query lines up with the last key (for Nq == Nk: j <= i); a
+ *     masked key is excluded outright.  Causal calls need Nq <= Nk, so every
+ *     row keeps at least key 0.
  *   - LSE_i = m_i + ln(l_i) over the scaled, masked scores (natural log).
  * Inputs are float32 arrays (bf16 data is widened exactly before the call);
  * every product and sum is carried in IEEE double, no fast-math.
@@ -28,19 +30,19 @@
 #include <omp.h>
 #endif
 
-/* One query row: flat row index r = (b*H + h)*N + i.  Writes d values of O
- * and one LSE.  `s` is a caller-provided scratch row of N doubles. */
+/* One query row: flat row index r = (b*H + h)*Nq + i.  Writes d values of O
+ * and one LSE.  `s` is a caller-provided scratch row of Nk doubles. */
 static void oracle_row(const float* q, const float* k, const float* v,
-                       int64_t H, int64_t N, int64_t d, double scale,
+                       int64_t Nq, int64_t Nk, int64_t d, double scale,
                        int causal, int64_t r, double* s, double* o_row,
                        double* lse_out) {
-  const int64_t bh = r / N;          /* (b*H + h) */
-  const int64_t i = r % N;           /* query position inside the head */
+  const int64_t bh = r / Nq;         /* (b*H + h) */
+  const int64_t i = r % Nq;          /* query position inside the head */
   const float* qi = q + r * d;
-  const float* kh = k + bh * N * d;
-  const float* vh = v + bh * N * d;
-  const int64_t nkeys = causal ? (i + 1) : N;   /* keys j with j <= i */
-  (void)H;
+  const float* kh = k + bh * Nk * d;
+  const float* vh = v + bh * Nk * d;
+  /* keys j with j <= i + (Nk - Nq) when causal */
+  const int64_t nkeys = causal ? (i + (Nk - Nq) + 1) : Nk;
 
   /* step 1: scores s_j = scale * <q_i, k_j> */
   double m = -INFINITY;
@@ -68,16 +70,18 @@ static void oracle_row(const float* q, const float* k, const float* v,
   *lse_out = m + log(l);
 }
 
-/* Attention over the rows listed in `rows` (flat indices into [B,H,N]);
- * rows == NULL means every row, in order.  O is [nrows, d], LSE [nrows].
- * Returns 0 on success, 1 on a bad argument, 2 if scratch allocation fails. */
+/* Attention of q [B,H,Nq,d] over k, v [B,H,Nk,d] for the query rows listed
+ * in `rows` (flat indices into [B,H,Nq]); rows == NULL means every row, in
+ * order.  O is [nrows, d], LSE [nrows].  Returns 0 on success, 1 on a bad
+ * argument (including causal with Nq > Nk), 2 if scratch allocation fails. */
 int oracle_attn_f64(const float* q, const float* k, const float* v,
-                    int64_t B, int64_t H, int64_t N, int64_t d, double scale,
-                    int causal, const int64_t* rows, int64_t nrows,
+                    int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
+                    double scale, int causal, const int64_t* rows, int64_t nrows,
                     double* O, double* LSE) {
-  if (!q || !k || !v || !O || !LSE || B < 1 || H < 1 || N < 1 || d < 1)
+  if (!q || !k || !v || !O || !LSE || B < 1 || H < 1 || Nq < 1 || Nk < 1 || d < 1)
     return 1;
-  const int64_t total = B * H * N;
+  if (causal && Nq > Nk) return 1;
+  const int64_t total = B * H * Nq;
   if (!rows) nrows = total;
   if (nrows < 0) return 1;
   for (int64_t t = 0; t < nrows && rows; ++t)
@@ -85,7 +89,7 @@ int oracle_attn_f64(const float* q, const float* k, const float* v,
   int failed = 0;
 #pragma omp parallel
   {
-    double* s = (double*)malloc(sizeof(double) * (size_t)N);
+    double* s = (double*)malloc(sizeof(double) * (size_t)Nk);
     if (!s) {
 #pragma omp atomic write
       failed = 1;
@@ -93,7 +97,7 @@ int oracle_attn_f64(const float* q, const float* k, const float* v,
 #pragma omp for schedule(dynamic, 16)
       for (int64_t t = 0; t < nrows; ++t) {
         const int64_t r = rows ? rows[t] : t;
-        oracle_row(q, k, v, H, N, d, scale, causal, r, s, O + t * d, LSE + t);
+        oracle_row(q, k, v, Nq, Nk, d, scale, causal, r, s, O + t * d, LSE + t);
       }
       free(s);
     }

@@ -355,3 +355,58 @@ def test_c_and_numpy_oracles_agree_on_workloads():
         On, Ln = oracle.attention_np(x["q"], x["k"], x["v"], w.scale, w.causal)
         assert np.abs(Oc - On).max() < 1e-12
         assert np.abs(Lc - Ln).max() < 1e-12
+
+
+# --------------------------------------------------------------- Nq != Nk
+def test_rectangular_rows_equal_last_rows_of_square_problem():
+    """Query rows Q' = the last Nq rows of a square problem's Q: for both
+    masks, every row of (Q', K, V) equals the matching last row of the square
+    problem (causal aligns the last query with the last key)."""
+    B, H, Nk, d = 1, 2, 37, 8
+    q = _rand((B, H, Nk, d), 70)
+    k = _rand((B, H, Nk, d), 71)
+    v = _rand((B, H, Nk, d), 72)
+    for Nq in (1, 5, 36, 37):
+        for causal in (False, True):
+            O_sq, L_sq = oracle.attention_c(q, k, v, 0.4, causal)
+            for f in (oracle.attention_c, oracle.attention_np):
+                O, L = f(q[:, :, Nk - Nq:].copy(), k, v, 0.4, causal)
+                assert np.abs(O - O_sq[:, :, Nk - Nq:]).max() < 1e-13
+                assert np.abs(L - L_sq[:, :, Nk - Nq:]).max() < 1e-13
+
+
+def test_single_query_causal_sees_every_key():
+    B, H, Nk, d = 2, 1, 50, 4
+    q = _rand((B, H, 1, d), 73)
+    k = _rand((B, H, Nk, d), 74)
+    v = _rand((B, H, Nk, d), 75)
+    Oc, Lc = oracle.attention_c(q, k, v, 0.7, True)
+    On, Ln = oracle.attention_c(q, k, v, 0.7, False)
+    assert np.array_equal(Oc, On) and np.array_equal(Lc, Ln)
+
+
+@pytest.mark.parametrize("Nq,Nk", [(1, 7), (3, 8), (6, 6)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_brute_force_rectangular(Nq, Nk, causal):
+    d = 3
+    q = _rand((1, 1, Nq, d), 80 + Nq)
+    k = _rand((1, 1, Nk, d), 90 + Nk)
+    v = _rand((1, 1, Nk, d), 95 + Nk)
+    ql, kl, vl = q[0, 0].tolist(), k[0, 0].tolist(), v[0, 0].tolist()
+    for f in (oracle.attention_c, oracle.attention_np):
+        O, L = f(q, k, v, 0.8, causal)
+        for i in range(Nq):
+            js = range(i + Nk - Nq + 1) if causal else range(Nk)
+            e = {j: math.exp(0.8 * sum(ql[i][c] * kl[j][c] for c in range(d))) for j in js}
+            z = sum(e.values())
+            ref = [sum(e[j] * vl[j][c] for j in js) / z for c in range(d)]
+            assert np.abs(O[0, 0, i] - np.array(ref)).max() < 1e-13
+            assert abs(L[0, 0, i] - math.log(z)) < 1e-13
+
+
+def test_causal_needs_enough_keys():
+    q = _rand((1, 1, 4, 2), 1)
+    k = _rand((1, 1, 3, 2), 2)
+    for f in (oracle.attention_c, oracle.attention_np):
+        with pytest.raises((ValueError, RuntimeError)):
+            f(q, k, k, 1.0, True)
