@@ -18,6 +18,12 @@ causal.  Also reported:
   cpu_baseline  the fp64 CPU oracle timed on a bounded sample of the same
                 workload's query rows, on this host's cores.
 
+--splitkv runs the workload through fa_fwd_splitkv (keys cut into the
+library's suggested number of chunks, then merged) instead of fa_fwd.
+--decode NK times single-query decoding instead: B=1, H=32, d=128, one
+query row against NK keys through fa_fwd_splitkv, reported as GB/s of K/V
+read (the path is bound by HBM there).
+
 --copy-bytes S runs only a plain device-to-device copy of S bytes (used to
 calibrate the FETCH_SIZE / WRITE_SIZE counters) and exits.
 
@@ -205,6 +211,41 @@ def summarize(out_dir, workload_name):
                       "traffic_bytes": rd + wr, "read": rd, "write": wr}))
 
 
+def decode_bench(fa, args):
+    """One query row per head against NK keys: the K/V read dominates."""
+    import torch
+    dev = torch.device("cuda:0")
+    B, H, d, nk = 1, 32, 128, args.decode
+    g = torch.Generator(device=dev).manual_seed(5)
+    q = torch.randn((B, H, 1, d), device=dev, generator=g).to(torch.bfloat16)
+    k = torch.randn((B, H, nk, d), device=dev, generator=g).to(torch.bfloat16)
+    v = torch.randn((B, H, nk, d), device=dev, generator=g).to(torch.bfloat16)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, 1), dtype=torch.float32, device=dev)
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    splits = fa.fa_fwd_splitkv_num_splits(B, H, 1, nk, cus)
+    ws = torch.empty(fa.fa_fwd_splitkv_workspace_size(B, H, 1, d, splits), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    a = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), B, H, 1, nk, d,
+         float(1 / np.sqrt(d)), 1, splits, ws.data_ptr(), ws.numel(), stream.cuda_stream)
+    for _ in range(args.warmup):
+        assert fa.fa_fwd_splitkv(*a) == 0
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(args.steps):
+        fa.fa_fwd_splitkv(*a)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / args.steps
+    kv_bytes = 2 * B * H * nk * d * 2
+    print(json.dumps({"metric": "decode K/V read GB/s (1 query row, causal, fa_fwd_splitkv)",
+                      "value": round(kv_bytes / (ms * 1e-3) / 1e9, 1), "unit": "GB/s",
+                      "ms_per_step": round(ms, 4), "steps": args.steps, "warmup": args.warmup,
+                      "config": {"workload": "decode", "B": B, "H": H, "Nq": 1, "Nk": nk, "d": d,
+                                 "splits": splits}, "peak_hbm_GBps": 8000}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -214,6 +255,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-bytes", type=int, default=0)
     ap.add_argument("--summarize", metavar="DIR", default=None)
+    ap.add_argument("--splitkv", action="store_true")
+    ap.add_argument("--decode", type=int, default=0, metavar="NK")
     args = ap.parse_args()
 
     if args.summarize:
@@ -237,6 +280,10 @@ def main():
     import io_aware_softmax_fwd_amd as fa
     from io_aware_softmax_fwd_amd import workloads as W
 
+    if args.decode:
+        decode_bench(fa, args)
+        return
+
     w = W.WORKLOADS[args.workload]
     x = W.make_inputs(w)
     dev = torch.device("cuda:0")
@@ -253,6 +300,18 @@ def main():
     f = fa.fa_fwd if w.dtype == "bf16" else fa.fa_fwd_f32
     call_args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
                  w.B, w.H, w.N, w.d, w.scale, int(w.causal), stream.cuda_stream)
+
+    if args.splitkv:
+        if w.dtype != "bf16":
+            raise SystemExit("--splitkv needs a bf16 workload")
+        cus = torch.cuda.get_device_properties(dev).multi_processor_count
+        splits = fa.fa_fwd_splitkv_num_splits(w.B, w.H, w.N, w.N, cus)
+        ws = torch.empty(fa.fa_fwd_splitkv_workspace_size(w.B, w.H, w.N, w.d, splits),
+                         dtype=torch.uint8, device=dev)
+        f = fa.fa_fwd_splitkv
+        call_args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                     w.B, w.H, w.N, w.N, w.d, w.scale, int(w.causal), splits, ws.data_ptr(),
+                     ws.numel(), stream.cuda_stream)
 
     def step():
         st = f(*call_args)
@@ -296,7 +355,8 @@ def main():
         "data": "synthetic (seeded N(0,1) draws, bf16-rounded)",
         "pct_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
-                   "causal": w.causal, "amplified_rows": w.amplify, "flops": w.flops},
+                   "causal": w.causal, "amplified_rows": w.amplify, "flops": w.flops,
+                   "entry_point": "fa_fwd_splitkv" if args.splitkv else f.__name__},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic, "kernel_ms": round(kernel_ms, 4),

@@ -32,6 +32,7 @@
 #ifndef FA_FWD_H
 #define FA_FWD_H
 
+#include <stddef.h>
 #include <hip/hip_runtime_api.h>
 
 #ifdef __cplusplus
@@ -47,7 +48,9 @@ enum fa_status {
   FA_ERR_ALIGN = 5,          /* a pointer is not 16-byte aligned               */
   FA_ERR_HIP = 6,            /* the HIP runtime refused the launch             */
   FA_ERR_CAUSAL = 7,         /* causal flag other than 0 or 1                  */
-  FA_ERR_ALIAS = 8           /* O or LSE overlaps an input or each other       */
+  FA_ERR_ALIAS = 8,          /* an output or the workspace overlaps a buffer   */
+  FA_ERR_WORKSPACE = 9,      /* workspace NULL or smaller than required        */
+  FA_ERR_SPLITS = 10         /* num_splits outside 1..128                      */
 };
 
 /*
@@ -79,6 +82,42 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
 int fa_fwd_f32(const float* q, const float* k, const float* v, float* o,
                float* lse, int B, int H, int N, int d, float scale,
                int causal, hipStream_t stream);
+
+/*
+ * Key-split attention forward (bf16), for grids too small to fill the GPU
+ * and for decode-shaped calls.  The keys of every query tile are cut into
+ * `num_splits` chunks handled by separate workgroups; each writes its own
+ * normalised O and LSE to `workspace`, and a merge kernel combines them with
+ * LSE = log sum_s exp(LSE_s), O = sum_s exp(LSE_s - LSE) O_s -- the
+ * online-softmax merge applied to whole chunks, as FlashDecoding does for
+ * decoding (zzszmyf.github.io notes "FlashAttention 原理是什么", sections 5
+ * and 12.1).  Results equal fa_fwd's up to rounding order.
+ *   q, o      : [B,H,Nq,d] bf16;  k, v : [B,H,Nk,d] bf16;  lse : [B,H,Nq] fp32.
+ *   Nq, Nk    : query rows and keys, >= 1.  Causal aligns the last query with
+ *               the last key: query i attends keys j <= i + Nk - Nq, so causal
+ *               calls need Nq <= Nk (Nq == Nk is the square problem).
+ *   num_splits: 1..128 chunks (fa_fwd_splitkv_num_splits suggests one).
+ *   workspace : device buffer of at least fa_fwd_splitkv_workspace_size(...)
+ *               bytes, 16-byte aligned, owned by the caller, overlapping no
+ *               other argument; its contents are scratch (nothing is kept
+ *               between calls, and calls sharing one workspace must not run
+ *               concurrently).
+ * Errors as for fa_fwd, plus FA_ERR_SHAPE for causal with Nq > Nk,
+ * FA_ERR_SPLITS and FA_ERR_WORKSPACE.  Two kernels are queued on `stream`.
+ */
+int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
+                   int B, int H, int Nq, int Nk, int d, float scale, int causal,
+                   int num_splits, void* workspace, size_t workspace_bytes,
+                   hipStream_t stream);
+
+/* Bytes of workspace fa_fwd_splitkv needs for these sizes; 0 if an
+ * argument is out of range.  Host only, no HIP call. */
+size_t fa_fwd_splitkv_workspace_size(int B, int H, int Nq, int d, int num_splits);
+
+/* A chunk count that gives about four workgroups per CU on a GPU with
+ * num_cus compute units (<= 0 means 256), keeping chunks of at least four
+ * 64-key tiles.  Host only, no HIP call. */
+int fa_fwd_splitkv_num_splits(int B, int H, int Nq, int Nk, int num_cus);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* fa_strerror(int status);

@@ -7,9 +7,15 @@ or cannot be loaded, every call raises.
 Low level (same names and arguments as the C functions, raw pointers):
     fa_fwd(q, k, v, o, lse, B, H, N, d, scale, causal, stream) -> status
     fa_fwd_f32(...)                                            -> status
+    fa_fwd_splitkv(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal,
+                   num_splits, workspace, workspace_bytes, stream) -> status
+    fa_fwd_splitkv_workspace_size(B, H, Nq, d, num_splits)     -> bytes
+    fa_fwd_splitkv_num_splits(B, H, Nq, Nk, num_cus)           -> count
     fa_strerror(status)                                        -> str
 High level (torch tensors on a ROCm device):
     fwd(q, k, v, scale=None, causal=False, out=None, lse=None) -> (o, lse)
+    fwd_splitkv(q, k, v, scale=None, causal=False, num_splits=None,
+                workspace=None)                                -> (o, lse)
 """
 import ctypes
 import math
@@ -26,8 +32,11 @@ FA_ERR_ALIGN = 5
 FA_ERR_HIP = 6
 FA_ERR_CAUSAL = 7
 FA_ERR_ALIAS = 8
+FA_ERR_WORKSPACE = 9
+FA_ERR_SPLITS = 10
 
-EXPORTED = ("fa_fwd", "fa_fwd_f32", "fa_strerror")
+EXPORTED = ("fa_fwd", "fa_fwd_f32", "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_size",
+            "fa_fwd_splitkv_num_splits", "fa_strerror")
 
 _lib = None
 
@@ -53,6 +62,14 @@ def load():
         f = getattr(lib, name)
         f.restype = ctypes.c_int
         f.argtypes = args
+    lib.fa_fwd_splitkv.restype = ctypes.c_int
+    lib.fa_fwd_splitkv.argtypes = ([ctypes.c_void_p] * 5 + [ctypes.c_int] * 5 +
+                                   [ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                    ctypes.c_size_t, ctypes.c_void_p])
+    lib.fa_fwd_splitkv_workspace_size.restype = ctypes.c_size_t
+    lib.fa_fwd_splitkv_workspace_size.argtypes = [ctypes.c_int] * 5
+    lib.fa_fwd_splitkv_num_splits.restype = ctypes.c_int
+    lib.fa_fwd_splitkv_num_splits.argtypes = [ctypes.c_int] * 5
     lib.fa_strerror.restype = ctypes.c_char_p
     lib.fa_strerror.argtypes = [ctypes.c_int]
     _lib = lib
@@ -65,6 +82,20 @@ def fa_fwd(q, k, v, o, lse, B, H, N, d, scale, causal, stream):
 
 def fa_fwd_f32(q, k, v, o, lse, B, H, N, d, scale, causal, stream):
     return load().fa_fwd_f32(q, k, v, o, lse, B, H, N, d, scale, causal, stream)
+
+
+def fa_fwd_splitkv(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, num_splits, workspace,
+                   workspace_bytes, stream):
+    return load().fa_fwd_splitkv(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, num_splits,
+                                 workspace, workspace_bytes, stream)
+
+
+def fa_fwd_splitkv_workspace_size(B, H, Nq, d, num_splits):
+    return int(load().fa_fwd_splitkv_workspace_size(B, H, Nq, d, num_splits))
+
+
+def fa_fwd_splitkv_num_splits(B, H, Nq, Nk, num_cus):
+    return int(load().fa_fwd_splitkv_num_splits(B, H, Nq, Nk, num_cus))
 
 
 def fa_strerror(status):
@@ -110,4 +141,44 @@ def fwd(q, k, v, scale=None, causal=False, out=None, lse=None, stream=None):
            B, H, N, d, float(scale), int(bool(causal)), stream)
     if st != FA_OK:
         raise FaError(st, f.__name__)
+    return out, lse
+
+
+def fwd_splitkv(q, k, v, scale=None, causal=False, num_splits=None, workspace=None,
+                out=None, lse=None, stream=None):
+    """Key-split attention forward of bf16 torch tensors: q [B,H,Nq,d],
+    k and v [B,H,Nk,d] (contiguous, on the GPU).  num_splits defaults to the
+    library's suggestion for this GPU; workspace (a uint8 device tensor) is
+    allocated here if not given.  Returns (o, lse)."""
+    import torch
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor):
+            raise TypeError("%s must be a torch.Tensor" % name)
+        if t.device.type != "cuda" or not t.is_contiguous() or t.dim() != 4:
+            raise ValueError("%s must be a contiguous 4-D GPU tensor" % name)
+        if t.dtype != torch.bfloat16:
+            raise TypeError("%s must be bfloat16" % name)
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    if k.shape != (B, H, Nk, d) or v.shape != k.shape:
+        raise ValueError("k and v must be [B, H, Nk, d] with q's B, H and d")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if num_splits is None:
+        cus = torch.cuda.get_device_properties(q.device).multi_processor_count
+        num_splits = fa_fwd_splitkv_num_splits(B, H, Nq, Nk, cus)
+    need = fa_fwd_splitkv_workspace_size(B, H, Nq, d, num_splits)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    st = fa_fwd_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                        B, H, Nq, Nk, d, float(scale), int(bool(causal)), int(num_splits),
+                        workspace.data_ptr(), workspace.numel() * workspace.element_size(), stream)
+    if st != FA_OK:
+        raise FaError(st, "fa_fwd_splitkv")
     return out, lse

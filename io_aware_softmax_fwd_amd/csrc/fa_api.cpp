@@ -6,6 +6,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "fa_fwd.h"
 #include "fa_internal.h"
 
@@ -14,6 +16,7 @@ namespace {
 // Largest supported problem: element offsets stay far inside int64 and the
 // 1-D grid (query tiles x heads) inside 2^31 workgroups.
 constexpr int64_t kMaxElems = int64_t(1) << 40;
+constexpr int kMaxSplits = 128;
 
 bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
 
@@ -44,6 +47,38 @@ int validate(const void* q, const void* k, const void* v, const void* o, const f
   return FA_OK;
 }
 
+int validate_split(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                   int B, int H, int Nq, int Nk, int d, float scale, int causal, int splits,
+                   const void* ws, size_t ws_bytes) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+  if (B < 1 || H < 1 || Nq < 1 || Nk < 1) return FA_ERR_SHAPE;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED_D;
+  const int64_t qrows = (int64_t)B * H * Nq, krows = (int64_t)B * H * Nk;
+  if (qrows * d >= kMaxElems || krows * d >= kMaxElems) return FA_ERR_SHAPE;
+  if ((int64_t)Nk * d * 2 >= (int64_t(1) << 31) || (int64_t)Nq * d * 2 >= (int64_t(1) << 31))
+    return FA_ERR_SHAPE;
+  if (!(scale > 0.f) || !isfinite(scale)) return FA_ERR_SCALE;
+  if (causal != 0 && causal != 1) return FA_ERR_CAUSAL;
+  if (causal && Nq > Nk) return FA_ERR_SHAPE;
+  if (splits < 1 || splits > kMaxSplits) return FA_ERR_SPLITS;
+  const int64_t n_qtiles = (Nq + 127) / 128;
+  if (n_qtiles * splits * B * H >= (int64_t(1) << 31)) return FA_ERR_SHAPE;
+  if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(o) || misaligned(lse))
+    return FA_ERR_ALIGN;
+  const fa::SplitLayout L = fa::splitkv_layout(B, H, Nq, d, splits);
+  if (!ws || (int64_t)ws_bytes < L.total) return FA_ERR_WORKSPACE;
+  if (misaligned(ws)) return FA_ERR_ALIGN;
+  const int64_t qb = qrows * d * 2, kb = krows * d * 2, lb = qrows * 4;
+  if (overlap(o, qb, q, qb) || overlap(o, qb, k, kb) || overlap(o, qb, v, kb) ||
+      overlap(lse, lb, q, qb) || overlap(lse, lb, k, kb) || overlap(lse, lb, v, kb) ||
+      overlap(lse, lb, o, qb))
+    return FA_ERR_ALIAS;
+  if (overlap(ws, L.total, q, qb) || overlap(ws, L.total, k, kb) || overlap(ws, L.total, v, kb) ||
+      overlap(ws, L.total, o, qb) || overlap(ws, L.total, lse, lb))
+    return FA_ERR_ALIAS;
+  return FA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -64,6 +99,33 @@ int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* 
   return fa::launch_fwd_f32(p, stream) == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
+size_t fa_fwd_splitkv_workspace_size(int B, int H, int Nq, int d, int num_splits) {
+  if (B < 1 || H < 1 || Nq < 1 || (d != 64 && d != 128) || num_splits < 1 || num_splits > kMaxSplits)
+    return 0;
+  return (size_t)fa::splitkv_layout(B, H, Nq, d, num_splits).total;
+}
+
+int fa_fwd_splitkv_num_splits(int B, int H, int Nq, int Nk, int num_cus) {
+  if (B < 1 || H < 1 || Nq < 1 || Nk < 1) return 1;
+  if (num_cus < 1) num_cus = 256;
+  // Aim for four workgroups per CU (two resident, two queued) while keeping
+  // at least four 64-key tiles per chunk.
+  const int64_t base = (int64_t)((Nq + 127) / 128) * B * H;
+  const int64_t want = ((int64_t)4 * num_cus + base - 1) / base;
+  const int64_t most = std::max<int64_t>(1, ((Nk + 63) / 64) / 4);
+  return (int)std::max<int64_t>(1, std::min<int64_t>(std::min<int64_t>(want, most), kMaxSplits));
+}
+
+int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                   int Nq, int Nk, int d, float scale, int causal, int num_splits, void* workspace,
+                   size_t workspace_bytes, hipStream_t stream) {
+  const int st = validate_split(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, num_splits,
+                                workspace, workspace_bytes);
+  if (st != FA_OK) return st;
+  const fa::SplitProblem p{q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, num_splits, workspace};
+  return fa::launch_fwd_bf16_splitkv(p, stream) == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 const char* fa_strerror(int status) {
   switch (status) {
     case FA_OK: return "success";
@@ -74,7 +136,9 @@ const char* fa_strerror(int status) {
     case FA_ERR_ALIGN: return "pointers must be 16-byte aligned";
     case FA_ERR_HIP: return "the HIP runtime rejected the kernel launch";
     case FA_ERR_CAUSAL: return "causal must be 0 or 1";
-    case FA_ERR_ALIAS: return "O or LSE overlaps an input or each other";
+    case FA_ERR_ALIAS: return "an output or the workspace overlaps another buffer";
+    case FA_ERR_WORKSPACE: return "workspace missing or smaller than the size query returns";
+    case FA_ERR_SPLITS: return "num_splits must be between 1 and 128";
     default: return "unknown status";
   }
 }

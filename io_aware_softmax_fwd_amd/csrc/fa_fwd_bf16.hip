@@ -111,14 +111,19 @@ __device__ __forceinline__ int dma_offset(int slot, int stride) {
   return r * (2 * D) + 16 * cc;
 }
 
-template <int D, int QB, bool CAUSAL>
+// SPLIT: the workgroup covers one chunk of the keys and may meet rows that
+// have no valid key in it; such rows keep m = -inf and l = 0.
+template <int D, int QB, bool CAUSAL, bool SPLIT>
 struct Fwd {
   static constexpr int KS = D / 16, DB = D / 32, KB = kKeys / 32, PS = kKeys / 16;
   static constexpr int WR = 32 * QB;        // query rows per wave
 
   const unsigned short* kh;
   const unsigned short* vh;
-  int N, wave, l32, hl, qw;
+  int N;                  // keys (Nk)
+  int Nq;                 // query rows
+  int coff;               // causal offset Nk - Nq: query i sees keys j <= i + coff
+  int wave, l32, hl, qw;
   float c, thr;
   bf16x8 qf[QB][KS];      // Q fragments (B operand of S^T = K Q^T), per 32-row block
   f32x16 acc[QB][DB];     // O^T accumulators: lane holds query l%32 of each block
@@ -174,8 +179,8 @@ struct Fwd {
   template <bool MASK>
   __device__ void softmax(int qb, f32x16 (&s)[KB], bf16x8 (&pf)[PS], int k0) {
     if constexpr (MASK) {
-      // key = k0 + 32*kb + (r&3) + 8*(r>>2) + 4*hl must be <= min(qi, N-1)
-      const int lim = (CAUSAL ? min(qi(qb), N - 1) : N - 1) - k0 - 4 * hl;
+      // key = k0 + 32*kb + (r&3) + 8*(r>>2) + 4*hl must be <= min(qi+coff, N-1)
+      const int lim = (CAUSAL ? min(qi(qb) + coff, N - 1) : N - 1) - k0 - 4 * hl;
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
@@ -194,7 +199,9 @@ struct Fwd {
     if (__builtin_amdgcn_ballot_w64(upd)) {
       asm volatile("" ::: "memory");   // keep this a taken/skipped branch
       const float m_new = upd ? mx : m[qb];
-      const float alpha = __builtin_amdgcn_exp2f((m[qb] - m_new) * c);   // 1 if kept, 0 at start
+      // 0 at the start (m = -inf); exactly 1 for rows that keep their offset
+      // (also when that offset is still -inf, which the key-split path meets)
+      const float alpha = upd ? __builtin_amdgcn_exp2f((m[qb] - m_new) * c) : 1.f;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -202,7 +209,9 @@ struct Fwd {
       l[qb] *= alpha;
       m[qb] = m_new;
     }
-    const float mc = m[qb] * c;
+    // A split chunk can hold no valid key for a row (m still -inf): its
+    // probabilities must come out 0, not exp2(-inf + inf).
+    const float mc = (SPLIT && m[qb] == -INFINITY) ? 0.f : m[qb] * c;
     // Probabilities, rounded to bf16 for the product; the row sum is taken
     // over the same rounded values (two per v_dot2_f32_bf16), so numerator
     // and denominator see identical weights.
@@ -276,32 +285,36 @@ struct Fwd {
   // whole step to land), consume tile j, wait and synchronise.
   // PAR = j & 1 selects the buffers at compile time.
   template <bool MASK, int PAR>
-  __device__ void step(int j, int n_tiles) {
+  __device__ void step(int j, int t_end) {
     const int k0 = j * kKeys;
-    if (j + 1 < n_tiles) {
+    if (j + 1 < t_end) {
       issue<false, PAR ^ 1>(k0 + kKeys);
       issue<true, PAR ^ 1>(k0 + kKeys);
     }
     // Causal: a wave whose last query precedes the tile's first key has
     // nothing to do here or later; the barrier below stays unconditional.
-    if (!MASK || !CAUSAL || k0 <= qw + WR - 1) consume<MASK, PAR>(k0);
+    if (!MASK || !CAUSAL || k0 <= qw + WR - 1 + coff) consume<MASK, PAR>(k0);
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
     __builtin_amdgcn_s_barrier();
   }
 };
 
-template <int D, int QB, bool CAUSAL>
+// One workgroup per (query tile, key chunk, batch*head).  Without SPLIT the
+// single chunk is every key and O/LSE are written directly; with SPLIT the
+// chunk's own normalised O (fp32) and LSE go to opart/lpart for the merge.
+template <int D, int QB, bool CAUSAL, bool SPLIT>
 __global__ __launch_bounds__(kThreads, QB == 1 ? 2 : 1) void fwd_bf16_kernel(
     const unsigned short* __restrict__ q, const unsigned short* __restrict__ k,
     const unsigned short* __restrict__ v, unsigned short* __restrict__ o,
-    float* __restrict__ lse, int N, int BH, int n_qtiles, float scale) {
+    float* __restrict__ lse, int Nq, int Nk, int BH, int n_qtiles, float scale, int splits,
+    float* __restrict__ opart, float* __restrict__ lpart) {
   __shared__ __attribute__((aligned(1024))) unsigned char k_lds0[Cfg<D>::kTile];
   __shared__ __attribute__((aligned(1024))) unsigned char k_lds1[Cfg<D>::kTile];
   __shared__ __attribute__((aligned(1024))) unsigned char v_lds0[Cfg<D>::vTile];
   __shared__ __attribute__((aligned(1024))) unsigned char v_lds1[Cfg<D>::vTile];
   constexpr int KS = D / 16, DB = D / 32;
   constexpr int BR = 32 * QB * kWaves;   // query rows per workgroup
-  using F = Fwd<D, QB, CAUSAL>;
+  using F = Fwd<D, QB, CAUSAL, SPLIT>;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -309,18 +322,23 @@ __global__ __launch_bounds__(kThreads, QB == 1 ? 2 : 1) void fwd_bf16_kernel(
   // vary fastest, so with B*H a multiple of 8 every tile of a head lands on
   // the same XCD and shares its L2.
   const int bh = blockIdx.x % BH;
-  const int qt = n_qtiles - 1 - (int)(blockIdx.x / BH);
+  const int rest = blockIdx.x / BH;
+  const int split = SPLIT ? rest % splits : 0;
+  const int qt = n_qtiles - 1 - (SPLIT ? rest / splits : rest);
   const int q0 = qt * BR;
-  const int64_t head = (int64_t)bh * N * D;
+  const int64_t qhead = (int64_t)bh * Nq * D;
+  const int64_t khead = (int64_t)bh * Nk * D;
 
   F f;
   f.kbuf[0] = k_lds0;
   f.kbuf[1] = k_lds1;
   f.vbuf[0] = v_lds0;
   f.vbuf[1] = v_lds1;
-  f.kh = k + head;
-  f.vh = v + head;
-  f.N = N;
+  f.kh = k + khead;
+  f.vh = v + khead;
+  f.N = Nk;
+  f.Nq = Nq;
+  f.coff = Nk - Nq;
   f.wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   f.l32 = lane & 31;
   f.hl = lane >> 5;
@@ -339,41 +357,53 @@ __global__ __launch_bounds__(kThreads, QB == 1 ? 2 : 1) void fwd_bf16_kernel(
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       u32x4 raw = {0u, 0u, 0u, 0u};
-      if (qi < N) raw = *reinterpret_cast<const u32x4*>(q + head + (int64_t)qi * D + 16 * ks + 8 * f.hl);
+      if (qi < Nq) raw = *reinterpret_cast<const u32x4*>(q + qhead + (int64_t)qi * D + 16 * ks + 8 * f.hl);
       f.qf[qb][ks] = __builtin_bit_cast(bf16x8, raw);
     }
   }
   f.setup_offsets(lane);
 
-  const int kv_end = CAUSAL ? min(N, q0 + BR) : N;
+  // Key tiles this workgroup's rows need, and its chunk [t0, t1) of them.
+  const int kv_end = CAUSAL ? min(Nk, q0 + BR + f.coff) : Nk;
   const int n_tiles = (kv_end + kKeys - 1) / kKeys;
-  // Tiles before n_full need no mask: every key is < N and, when causal,
-  // precedes the workgroup's first query.
-  const int n_full = CAUSAL ? min(q0, N / kKeys * kKeys) / kKeys : N / kKeys;
+  const int t0 = SPLIT ? (int)((int64_t)split * n_tiles / splits) : 0;
+  const int t1 = SPLIT ? (int)((int64_t)(split + 1) * n_tiles / splits) : n_tiles;
+  // Tiles before n_full need no mask: every key is < Nk and, when causal,
+  // visible to the workgroup's first query.
+  const int n_full = CAUSAL ? min(q0 + f.coff + 1, Nk) / kKeys : Nk / kKeys;
 
-  f.template issue<false, 0>(0);
-  f.template issue<true, 0>(0);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-  int j = 0;
-  for (; j + 1 < n_full; j += 2) {
-    f.template step<false, 0>(j, n_tiles);
-    f.template step<false, 1>(j + 1, n_tiles);
-  }
-  if (j < n_full) f.template step<false, 0>(j++, n_tiles);
-  for (; j < n_tiles; ++j) {
-    if (j & 1) f.template step<true, 1>(j, n_tiles);
-    else       f.template step<true, 0>(j, n_tiles);
+  if (t0 < t1) {
+    f.template issue<false, 0>(t0 * kKeys);
+    f.template issue<true, 0>(t0 * kKeys);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    // buffer parity counts from t0
+    int j = t0;
+    const int full_end = max(t0, min(t1, n_full));
+    for (; j + 1 < full_end; j += 2) {
+      f.template step<false, 0>(j, t1);
+      f.template step<false, 1>(j + 1, t1);
+    }
+    if (j < full_end) {
+      f.template step<false, 0>(j, t1);
+      ++j;
+    }
+    for (; j < t1; ++j) {
+      if ((j - t0) & 1) f.template step<true, 1>(j, t1);
+      else              f.template step<true, 0>(j, t1);
+    }
   }
 
-  // Epilogue: O = acc / l in bf16 (round to nearest even), LSE = scale*m + ln l.
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const float l_tot = sum_across_halves(f.l[qb]);
     const int qi = f.qi(qb);
-    if (qi < N) {
+    if (qi >= Nq) continue;
+    const int64_t row = (int64_t)bh * Nq + qi;
+    if constexpr (!SPLIT) {
+      // O = acc / l in bf16 (round to nearest even), LSE = scale*m + ln l.
       const float inv = 1.f / l_tot;
-      unsigned short* orow = o + head + (int64_t)qi * D;
+      unsigned short* orow = o + qhead + (int64_t)qi * D;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -383,9 +413,60 @@ __global__ __launch_bounds__(kThreads, QB == 1 ? 2 : 1) void fwd_bf16_kernel(
                            pack_bf16x2(f.acc[qb][db][4 * g + 2] * inv, f.acc[qb][db][4 * g + 3] * inv)};
           *reinterpret_cast<u32x2*>(orow + dim) = w;
         }
-      if (f.hl == 0) lse[(int64_t)bh * N + qi] = f.m[qb] * scale + logf(l_tot);
+      if (f.hl == 0) lse[row] = f.m[qb] * scale + logf(l_tot);
+    } else {
+      // this chunk's normalised O and LSE; a row with no valid key in the
+      // chunk gets O = 0 and LSE = -inf (weight 0 in the merge)
+      const bool empty = !(l_tot > 0.f);
+      const float inv = empty ? 0.f : 1.f / l_tot;
+      const int64_t prow = (int64_t)split * BH * Nq + row;
+      float* orow = opart + prow * D;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int dim = 32 * db + 8 * g + 4 * f.hl;
+          const float4 w = {f.acc[qb][db][4 * g] * inv, f.acc[qb][db][4 * g + 1] * inv,
+                            f.acc[qb][db][4 * g + 2] * inv, f.acc[qb][db][4 * g + 3] * inv};
+          *reinterpret_cast<float4*>(orow + dim) = w;
+        }
+      if (f.hl == 0) lpart[prow] = empty ? -INFINITY : f.m[qb] * scale + logf(l_tot);
     }
   }
+}
+
+// Merge of the key chunks of every row: LSE = log sum_s exp(LSE_s) and
+// O = sum_s exp(LSE_s - LSE) O_s, the online-softmax merge applied to whole
+// chunks (zzszmyf.github.io notes, sections 5 and 12.1).  One thread per
+// (row, 8 head dims); chunk 0 always holds key 0, so the max is finite.
+template <int D>
+__global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ opart,
+                                                    const float* __restrict__ lpart,
+                                                    unsigned short* __restrict__ o,
+                                                    float* __restrict__ lse, int64_t rows,
+                                                    int splits) {
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t row = t / (D / 8);
+  const int c8 = (int)(t % (D / 8));
+  if (row >= rows) return;
+  float mx = -INFINITY;
+  for (int sp = 0; sp < splits; ++sp) mx = fmaxf(mx, lpart[(int64_t)sp * rows + row]);
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  float sum = 0.f;
+  for (int sp = 0; sp < splits; ++sp) {
+    const float ls = lpart[(int64_t)sp * rows + row];
+    const float w = ls == -INFINITY ? 0.f : expf(ls - mx);
+    sum += w;
+    const float4* src = reinterpret_cast<const float4*>(opart + ((int64_t)sp * rows + row) * D + 8 * c8);
+    const float4 a = src[0], b = src[1];
+    acc[0] += w * a.x; acc[1] += w * a.y; acc[2] += w * a.z; acc[3] += w * a.w;
+    acc[4] += w * b.x; acc[5] += w * b.y; acc[6] += w * b.z; acc[7] += w * b.w;
+  }
+  const float inv = 1.f / sum;
+  const u32x4 out = {pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv),
+                     pack_bf16x2(acc[4] * inv, acc[5] * inv), pack_bf16x2(acc[6] * inv, acc[7] * inv)};
+  *reinterpret_cast<u32x4*>(o + row * D + 8 * c8) = out;
+  if (c8 == 0) lse[row] = mx + logf(sum);
 }
 
 template <int D, int QB, bool CAUSAL>
@@ -394,10 +475,33 @@ hipError_t launch(const Problem& p, hipStream_t stream) {
   const int n_qtiles = (p.N + BR - 1) / BR;
   const int BH = p.B * p.H;
   const dim3 grid((unsigned)((int64_t)n_qtiles * BH)), block(kThreads);
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, QB, CAUSAL>), grid, block, 0, stream,
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, QB, CAUSAL, false>), grid, block, 0, stream,
                      static_cast<const unsigned short*>(p.q), static_cast<const unsigned short*>(p.k),
                      static_cast<const unsigned short*>(p.v), static_cast<unsigned short*>(p.o),
-                     p.lse, p.N, BH, n_qtiles, p.scale);
+                     p.lse, p.N, p.N, BH, n_qtiles, p.scale, 1, nullptr, nullptr);
+  return hipGetLastError();
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch_split(const SplitProblem& p, hipStream_t stream) {
+  constexpr int BR = 32 * kWaves;
+  const int n_qtiles = (p.Nq + BR - 1) / BR;
+  const int BH = p.B * p.H;
+  const SplitLayout L = splitkv_layout(p.B, p.H, p.Nq, p.d, p.splits);
+  float* opart = static_cast<float*>(p.workspace);
+  float* lpart = reinterpret_cast<float*>(static_cast<unsigned char*>(p.workspace) + L.lse_offset);
+  const dim3 grid((unsigned)((int64_t)n_qtiles * p.splits * BH)), block(kThreads);
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, 1, CAUSAL, true>), grid, block, 0, stream,
+                     static_cast<const unsigned short*>(p.q), static_cast<const unsigned short*>(p.k),
+                     static_cast<const unsigned short*>(p.v), nullptr, nullptr, p.Nq, p.Nk, BH,
+                     n_qtiles, p.scale, p.splits, opart, lpart);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t rows = (int64_t)BH * p.Nq;
+  const int64_t threads = rows * (D / 8);
+  const dim3 mgrid((unsigned)((threads + 255) / 256)), mblock(256);
+  hipLaunchKernelGGL((merge_kernel<D>), mgrid, mblock, 0, stream, opart, lpart,
+                     static_cast<unsigned short*>(p.o), p.lse, rows, p.splits);
   return hipGetLastError();
 }
 
@@ -414,6 +518,11 @@ hipError_t launch_fwd_bf16(const Problem& p, hipStream_t stream) {
   if (p.d == 64)
     return p.causal ? launch<64, FA_QB64, true>(p, stream) : launch<64, FA_QB64, false>(p, stream);
   return p.causal ? launch<128, FA_QB128, true>(p, stream) : launch<128, FA_QB128, false>(p, stream);
+}
+
+hipError_t launch_fwd_bf16_splitkv(const SplitProblem& p, hipStream_t stream) {
+  if (p.d == 64) return p.causal ? launch_split<64, true>(p, stream) : launch_split<64, false>(p, stream);
+  return p.causal ? launch_split<128, true>(p, stream) : launch_split<128, false>(p, stream);
 }
 
 }  // namespace fa

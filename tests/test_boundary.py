@@ -88,3 +88,43 @@ def test_missing_library_fails_loudly(monkeypatch):
     monkeypatch.setattr(fa.binding, "LIB_PATH", "/nonexistent/libfa_fwd.so")
     with pytest.raises(ImportError):
         fa.binding.fa_fwd(A, A, A, A, A, 1, 1, 1, 64, 1.0, 0, None)
+
+
+def _split_call(**kw):
+    args = dict(q=A, k=A + 8 * MB, v=A + 16 * MB, o=A + 24 * MB, lse=A + 32 * MB,
+                B=1, H=2, Nq=64, Nk=128, d=64, scale=0.125, causal=0, splits=2,
+                ws=A + 64 * MB, ws_bytes=1 << 24, stream=None)
+    args.update(kw)
+    return fa.fa_fwd_splitkv(args["q"], args["k"], args["v"], args["o"], args["lse"], args["B"],
+                             args["H"], args["Nq"], args["Nk"], args["d"], args["scale"],
+                             args["causal"], args["splits"], args["ws"], args["ws_bytes"],
+                             args["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), fa.FA_ERR_NULL), (dict(lse=None), fa.FA_ERR_NULL),
+    (dict(Nq=0), fa.FA_ERR_SHAPE), (dict(Nk=0), fa.FA_ERR_SHAPE),
+    (dict(causal=1, Nq=129, Nk=128), fa.FA_ERR_SHAPE),
+    (dict(d=80), fa.FA_ERR_UNSUPPORTED_D), (dict(scale=-1.0), fa.FA_ERR_SCALE),
+    (dict(causal=3), fa.FA_ERR_CAUSAL),
+    (dict(splits=0), fa.FA_ERR_SPLITS), (dict(splits=129), fa.FA_ERR_SPLITS),
+    (dict(ws=None), fa.FA_ERR_WORKSPACE), (dict(ws_bytes=100), fa.FA_ERR_WORKSPACE),
+    (dict(ws=A + 64 * MB + 8), fa.FA_ERR_ALIGN), (dict(v=A + 16 * MB + 4), fa.FA_ERR_ALIGN),
+    (dict(ws=A + 24 * MB), fa.FA_ERR_ALIAS), (dict(o=A + 8 * MB), fa.FA_ERR_ALIAS),
+])
+def test_splitkv_bad_arguments_rejected_on_host(kw, status):
+    assert _split_call(**kw) == status
+
+
+def test_splitkv_workspace_size_and_split_choice():
+    # o part: splits*rows*d*4 rounded to 256, then lse part rounded to 256
+    rows = 2 * 8 * 1024
+    assert fa.fa_fwd_splitkv_workspace_size(2, 8, 1024, 64, 4) == 4 * rows * 64 * 4 + 4 * rows * 4
+    assert fa.fa_fwd_splitkv_workspace_size(1, 1, 1, 128, 3) == 1536 + 256
+    assert fa.fa_fwd_splitkv_workspace_size(1, 1, 1, 96, 3) == 0
+    assert fa.fa_fwd_splitkv_workspace_size(1, 1, 1, 64, 0) == 0
+    # big grids need no split; small grids and long key runs get more
+    assert fa.fa_fwd_splitkv_num_splits(1, 32, 16384, 16384, 256) == 1
+    assert fa.fa_fwd_splitkv_num_splits(2, 8, 1024, 1024, 256) == 4
+    assert fa.fa_fwd_splitkv_num_splits(1, 8, 1, 32768, 256) == 128
+    assert fa.fa_fwd_splitkv_num_splits(1, 1, 1, 64, 256) == 1
