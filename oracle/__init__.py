@@ -5,7 +5,9 @@ CPU-baseline leg may import this package.  It shares no code with the GPU
 library (io_aware_softmax_fwd_amd): neither imports the other.
 
 What it computes, for every (b, h, i) with Q of layout [B, H, Nq, d] and
-K, V of layout [B, H, Nk, d] (Nq == Nk == N for the square problem):
+K, V of layout [B, Hkv, Nk, d] (Nq == Nk == N for the square problem;
+Hkv == H for ordinary multi-head attention, else query head h reads K/V
+head h // (H // Hkv)):
 
     s_j   = scale * <q_i, k_j>          j in J_i = {0..Nk-1}, or, if causal,
                                         {0..i + Nk - Nq} (the last query lines
@@ -55,7 +57,7 @@ def _load():
         lib.oracle_attn_f64.argtypes = [
             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
             ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
-            ctypes.c_double, ctypes.c_int, ctypes.c_void_p, ctypes.c_int64,
+            ctypes.c_int64, ctypes.c_double, ctypes.c_int, ctypes.c_void_p, ctypes.c_int64,
             ctypes.c_void_p, ctypes.c_void_p]
         lib.oracle_max_threads.restype = ctypes.c_int
         lib.oracle_max_threads.argtypes = []
@@ -76,17 +78,18 @@ def _as_f32(x):
 
 
 def attention_c(q, k, v, scale, causal, rows=None):
-    """fp64 attention of float32 inputs: q [B,H,Nq,d], k and v [B,H,Nk,d].
+    """fp64 attention of float32 inputs: q [B,H,Nq,d], k and v [B,Hkv,Nk,d].
 
     rows: optional 1-D array of flat query-row indices r = (b*H + h)*Nq + i.
     Returns (O, LSE) as float64: O [B,H,Nq,d] and LSE [B,H,Nq] when rows is
     None, else O [len(rows), d] and LSE [len(rows)].
     """
     q, k, v = _as_f32(q), _as_f32(k), _as_f32(v)
-    if k.shape != v.shape or q.shape[:2] != k.shape[:2] or q.shape[3] != k.shape[3]:
-        raise ValueError("q [B,H,Nq,d], k and v [B,H,Nk,d] expected")
+    if k.shape != v.shape or q.shape[0] != k.shape[0] or q.shape[3] != k.shape[3] \
+            or q.shape[1] % k.shape[1] != 0:
+        raise ValueError("q [B,H,Nq,d], k and v [B,Hkv,Nk,d] with Hkv dividing H expected")
     B, H, Nq, d = q.shape
-    Nk = k.shape[2]
+    Hkv, Nk = k.shape[1], k.shape[2]
     if causal and Nq > Nk:
         raise ValueError("causal attention needs Nq <= Nk")
     if rows is None:
@@ -98,7 +101,7 @@ def attention_c(q, k, v, scale, causal, rows=None):
     O = np.empty((nrows, d), dtype=np.float64)
     LSE = np.empty((nrows,), dtype=np.float64)
     rc = _load().oracle_attn_f64(
-        q.ctypes.data, k.ctypes.data, v.ctypes.data, B, H, Nq, Nk, d,
+        q.ctypes.data, k.ctypes.data, v.ctypes.data, B, H, Hkv, Nq, Nk, d,
         float(scale), int(bool(causal)),
         None if rows_arr is None else rows_arr.ctypes.data, nrows,
         O.ctypes.data, LSE.ctypes.data)
@@ -112,12 +115,16 @@ def attention_c(q, k, v, scale, causal, rows=None):
 def attention_np(q, k, v, scale, causal, block_rows=1024):
     """The same definition as attention_c, written with numpy fp64 matmuls.
 
-    Row blocks only bound memory; each row's softmax is taken whole.
+    Row blocks only bound memory; each row's softmax is taken whole.  Grouped
+    K/V heads are expanded by repeating each one H // Hkv times.
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
     B, H, Nq, d = q.shape
+    if k.shape[1] != H:
+        k = np.repeat(k, H // k.shape[1], axis=1)
+        v = np.repeat(v, H // v.shape[1], axis=1)
     Nk = k.shape[2]
     if causal and Nq > Nk:
         raise ValueError("causal attention needs Nq <= Nk")

@@ -14,6 +14,8 @@
  *
  * Readings of what the pages leave open:
  *   - S is scaled by `scale` before the softmax (the pages' demo omits it).
+ *   - grouped K/V heads: K and V carry Hkv heads, query head h reads K/V
+ *     head h / (H / Hkv) (Hkv == H is ordinary multi-head attention).
  *   - causal: key j takes part in query row i iff j <= i + (Nk - Nq), i.e.
  *     the last query lines up with the last key (for Nq == Nk: j <= i); a
  *     masked key is excluded outright.  Causal calls need Nq <= Nk, so every
@@ -33,14 +35,16 @@
 /* One query row: flat row index r = (b*H + h)*Nq + i.  Writes d values of O
  * and one LSE.  `s` is a caller-provided scratch row of Nk doubles. */
 static void oracle_row(const float* q, const float* k, const float* v,
-                       int64_t Nq, int64_t Nk, int64_t d, double scale,
-                       int causal, int64_t r, double* s, double* o_row,
+                       int64_t H, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d,
+                       double scale, int causal, int64_t r, double* s, double* o_row,
                        double* lse_out) {
   const int64_t bh = r / Nq;         /* (b*H + h) */
   const int64_t i = r % Nq;          /* query position inside the head */
+  const int64_t b = bh / H, h = bh % H;
+  const int64_t bkv = b * Hkv + h / (H / Hkv);   /* the K/V head it reads */
   const float* qi = q + r * d;
-  const float* kh = k + bh * Nk * d;
-  const float* vh = v + bh * Nk * d;
+  const float* kh = k + bkv * Nk * d;
+  const float* vh = v + bkv * Nk * d;
   /* keys j with j <= i + (Nk - Nq) when causal */
   const int64_t nkeys = causal ? (i + (Nk - Nq) + 1) : Nk;
 
@@ -70,16 +74,18 @@ static void oracle_row(const float* q, const float* k, const float* v,
   *lse_out = m + log(l);
 }
 
-/* Attention of q [B,H,Nq,d] over k, v [B,H,Nk,d] for the query rows listed
- * in `rows` (flat indices into [B,H,Nq]); rows == NULL means every row, in
- * order.  O is [nrows, d], LSE [nrows].  Returns 0 on success, 1 on a bad
- * argument (including causal with Nq > Nk), 2 if scratch allocation fails. */
+/* Attention of q [B,H,Nq,d] over k, v [B,Hkv,Nk,d] for the query rows
+ * listed in `rows` (flat indices into [B,H,Nq]); rows == NULL means every
+ * row, in order.  O is [nrows, d], LSE [nrows].  Returns 0 on success, 1 on
+ * a bad argument (including causal with Nq > Nk, or H not a multiple of
+ * Hkv), 2 if scratch allocation fails. */
 int oracle_attn_f64(const float* q, const float* k, const float* v,
-                    int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
+                    int64_t B, int64_t H, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d,
                     double scale, int causal, const int64_t* rows, int64_t nrows,
                     double* O, double* LSE) {
-  if (!q || !k || !v || !O || !LSE || B < 1 || H < 1 || Nq < 1 || Nk < 1 || d < 1)
+  if (!q || !k || !v || !O || !LSE || B < 1 || H < 1 || Hkv < 1 || Nq < 1 || Nk < 1 || d < 1)
     return 1;
+  if (H % Hkv != 0) return 1;
   if (causal && Nq > Nk) return 1;
   const int64_t total = B * H * Nq;
   if (!rows) nrows = total;
@@ -97,7 +103,7 @@ int oracle_attn_f64(const float* q, const float* k, const float* v,
 #pragma omp for schedule(dynamic, 16)
       for (int64_t t = 0; t < nrows; ++t) {
         const int64_t r = rows ? rows[t] : t;
-        oracle_row(q, k, v, Nq, Nk, d, scale, causal, r, s, O + t * d, LSE + t);
+        oracle_row(q, k, v, H, Hkv, Nq, Nk, d, scale, causal, r, s, O + t * d, LSE + t);
       }
       free(s);
     }

@@ -410,3 +410,32 @@ def test_causal_needs_enough_keys():
     for f in (oracle.attention_c, oracle.attention_np):
         with pytest.raises((ValueError, RuntimeError)):
             f(q, k, k, 1.0, True)
+
+
+# ------------------------------------------------------ grouped K/V heads
+@pytest.mark.parametrize("H,Hkv", [(8, 2), (8, 1), (6, 3), (4, 4)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_grouped_kv_heads(H, Hkv, causal):
+    """The C oracle's head mapping (h -> h // (H // Hkv)) against the numpy
+    oracle's explicit repetition of every K/V head, and each query head
+    against a one-head problem over its K/V head."""
+    B, Nq, Nk, d = 2, 9, 13, 4
+    q = _rand((B, H, Nq, d), 100 + H)
+    k = _rand((B, Hkv, Nk, d), 110 + Hkv)
+    v = _rand((B, Hkv, Nk, d), 120 + Hkv)
+    Oc, Lc = oracle.attention_c(q, k, v, 0.6, causal)
+    On, Ln = oracle.attention_np(q, k, v, 0.6, causal)
+    assert np.abs(Oc - On).max() < 1e-13 and np.abs(Lc - Ln).max() < 1e-13
+    g = H // Hkv
+    for b in range(B):
+        for h in range(H):
+            O1, L1 = oracle.attention_c(q[b:b + 1, h:h + 1], k[b:b + 1, h // g:h // g + 1],
+                                        v[b:b + 1, h // g:h // g + 1], 0.6, causal)
+            assert np.array_equal(O1[0, 0], Oc[b, h]) and np.array_equal(L1[0, 0], Lc[b, h])
+
+
+def test_grouped_kv_heads_must_divide():
+    q = _rand((1, 6, 4, 2), 1)
+    k = _rand((1, 4, 4, 2), 2)
+    with pytest.raises(ValueError):
+        oracle.attention_c(q, k, k, 1.0, False)
