@@ -23,6 +23,10 @@ library's suggested number of chunks, then merged) instead of fa_fwd.
 --decode NK times single-query decoding instead: B=1, H=32, d=128, one
 query row against NK keys through fa_fwd_splitkv, reported as GB/s of K/V
 read (the path is bound by HBM there).
+--hkv HKV gives K/V only HKV heads (grouped-query attention through
+fa_fwd_gqa; query head h reads K/V head h / (H/HKV)): with --decode the
+K/V bytes shrink by H/HKV; with a workload its K/V keep their first HKV
+heads (FLOPs unchanged).
 
 --copy-bytes S runs only a plain device-to-device copy of S bytes (used to
 calibrate the FETCH_SIZE / WRITE_SIZE counters) and exits.
@@ -72,7 +76,8 @@ def measured_traffic(workload_name):
 
 
 def cpu_baseline(x, w, target_s=15.0):
-    """Time the fp64 oracle on sampled query rows of the workload."""
+    """Time the fp64 oracle on sampled query rows of the workload (x holds
+    its q, k, v; k and v may carry fewer heads than q)."""
     import oracle
     rng = np.random.default_rng(12345)
     total_rows = w.B * w.H * w.N
@@ -216,34 +221,43 @@ def decode_bench(fa, args):
     import torch
     dev = torch.device("cuda:0")
     B, H, d, nk = 1, 32, 128, args.decode
+    hkv = args.hkv or H
     g = torch.Generator(device=dev).manual_seed(5)
     q = torch.randn((B, H, 1, d), device=dev, generator=g).to(torch.bfloat16)
-    k = torch.randn((B, H, nk, d), device=dev, generator=g).to(torch.bfloat16)
-    v = torch.randn((B, H, nk, d), device=dev, generator=g).to(torch.bfloat16)
+    k = torch.randn((B, hkv, nk, d), device=dev, generator=g).to(torch.bfloat16)
+    v = torch.randn((B, hkv, nk, d), device=dev, generator=g).to(torch.bfloat16)
     o = torch.empty_like(q)
     lse = torch.empty((B, H, 1), dtype=torch.float32, device=dev)
     cus = torch.cuda.get_device_properties(dev).multi_processor_count
-    splits = fa.fa_fwd_splitkv_num_splits(B, H, 1, nk, cus)
-    ws = torch.empty(fa.fa_fwd_splitkv_workspace_size(B, H, 1, d, splits), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
-    a = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), B, H, 1, nk, d,
-         float(1 / np.sqrt(d)), 1, splits, ws.data_ptr(), ws.numel(), stream.cuda_stream)
+    scale = float(1 / np.sqrt(d))
+    if args.hkv:
+        f = fa.fa_fwd_gqa
+        splits = fa.fa_fwd_gqa_num_splits(B, H, hkv, 1, nk, 1, cus)
+    else:
+        f = fa.fa_fwd_splitkv
+        splits = fa.fa_fwd_splitkv_num_splits(B, H, 1, nk, cus)
+    ws = torch.empty(fa.fa_fwd_splitkv_workspace_size(B, H, 1, d, splits), dtype=torch.uint8, device=dev)
+    ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr())
+    tail = (1, nk, d, scale, 1, splits, ws.data_ptr(), ws.numel(), stream.cuda_stream)
+    a = ptrs + ((B, H, hkv) if args.hkv else (B, H)) + tail
     for _ in range(args.warmup):
-        assert fa.fa_fwd_splitkv(*a) == 0
+        assert f(*a) == 0
     torch.cuda.synchronize()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     ev0.record(stream)
     for _ in range(args.steps):
-        fa.fa_fwd_splitkv(*a)
+        f(*a)
     ev1.record(stream)
     torch.cuda.synchronize()
     ms = ev0.elapsed_time(ev1) / args.steps
-    kv_bytes = 2 * B * H * nk * d * 2
-    print(json.dumps({"metric": "decode K/V read GB/s (1 query row, causal, fa_fwd_splitkv)",
+    kv_bytes = 2 * B * hkv * nk * d * 2
+    print(json.dumps({"metric": "decode K/V read GB/s (1 query row, causal, %s)" % f.__name__,
                       "value": round(kv_bytes / (ms * 1e-3) / 1e9, 1), "unit": "GB/s",
                       "ms_per_step": round(ms, 4), "steps": args.steps, "warmup": args.warmup,
-                      "config": {"workload": "decode", "B": B, "H": H, "Nq": 1, "Nk": nk, "d": d,
-                                 "splits": splits}, "peak_hbm_GBps": 8000}), flush=True)
+                      "config": {"workload": "decode", "B": B, "H": H, "Hkv": hkv, "Nq": 1,
+                                 "Nk": nk, "d": d, "splits": splits},
+                      "peak_hbm_GBps": 8000}), flush=True)
 
 
 def main():
@@ -257,6 +271,7 @@ def main():
     ap.add_argument("--summarize", metavar="DIR", default=None)
     ap.add_argument("--splitkv", action="store_true")
     ap.add_argument("--decode", type=int, default=0, metavar="NK")
+    ap.add_argument("--hkv", type=int, default=0, metavar="HKV")
     args = ap.parse_args()
 
     if args.summarize:
@@ -287,6 +302,13 @@ def main():
     w = W.WORKLOADS[args.workload]
     x = W.make_inputs(w)
     dev = torch.device("cuda:0")
+    hkv = args.hkv or w.H
+    if args.hkv:
+        if w.dtype != "bf16" or w.H % hkv != 0:
+            raise SystemExit("--hkv needs a bf16 workload and HKV dividing its H")
+        for name in ("k", "v"):
+            x[name] = np.ascontiguousarray(x[name][:, :hkv])
+            x[name + "_bits"] = np.ascontiguousarray(x[name + "_bits"][:, :hkv])
 
     def up(name):
         if w.dtype == "bf16":
@@ -301,7 +323,17 @@ def main():
     call_args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
                  w.B, w.H, w.N, w.d, w.scale, int(w.causal), stream.cuda_stream)
 
-    if args.splitkv:
+    if args.hkv:
+        cus = torch.cuda.get_device_properties(dev).multi_processor_count
+        splits = (fa.fa_fwd_gqa_num_splits(w.B, w.H, hkv, w.N, w.N, int(w.causal), cus)
+                  if args.splitkv else 1)
+        ws = torch.empty(max(1, fa.fa_fwd_splitkv_workspace_size(w.B, w.H, w.N, w.d, splits)),
+                         dtype=torch.uint8, device=dev)
+        f = fa.fa_fwd_gqa
+        call_args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                     w.B, w.H, hkv, w.N, w.N, w.d, w.scale, int(w.causal), splits, ws.data_ptr(),
+                     ws.numel(), stream.cuda_stream)
+    elif args.splitkv:
         if w.dtype != "bf16":
             raise SystemExit("--splitkv needs a bf16 workload")
         cus = torch.cuda.get_device_properties(dev).multi_processor_count
@@ -339,7 +371,10 @@ def main():
     ms_per_step = wall * 1e3 / args.steps
     value = w.flops / (ms_per_step * 1e-3) / 1e12
     achieved = w.flops / (kernel_ms * 1e-3) / 1e12
-    traffic = measured_traffic(w.name)
+    traffic = measured_traffic(w.name) if not (args.hkv or args.splitkv) else None
+    n_rows = w.B * w.H * w.N
+    alg_bytes = (w.algorithmic_bytes if not args.hkv else
+                 2 * n_rows * w.d * 2 + 2 * w.B * hkv * w.N * w.d * 2 + 4 * n_rows)
     line = {
         "metric": "fwd attention TFLOP/s (4BHN^2d, causal halved) + % bf16 MFMA peak, N=16K d=128",
         "value": round(value, 2),
@@ -354,13 +389,13 @@ def main():
         "dtype": w.dtype,
         "data": "synthetic (seeded N(0,1) draws, bf16-rounded)",
         "pct_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
-        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
-                   "causal": w.causal, "amplified_rows": w.amplify, "flops": w.flops,
-                   "entry_point": "fa_fwd_splitkv" if args.splitkv else f.__name__},
+        "config": {"workload": w.name + ("_hkv%d" % hkv if args.hkv else ""), "B": w.B, "H": w.H,
+                   "Hkv": hkv, "N": w.N, "d": w.d, "causal": w.causal,
+                   "amplified_rows": w.amplify, "flops": w.flops, "entry_point": f.__name__},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic, "kernel_ms": round(kernel_ms, 4),
-                     "algorithmic_bytes": w.algorithmic_bytes},
+                     "algorithmic_bytes": alg_bytes},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

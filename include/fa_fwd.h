@@ -50,7 +50,8 @@ enum fa_status {
   FA_ERR_CAUSAL = 7,         /* causal flag other than 0 or 1                  */
   FA_ERR_ALIAS = 8,          /* an output or the workspace overlaps a buffer   */
   FA_ERR_WORKSPACE = 9,      /* workspace NULL or smaller than required        */
-  FA_ERR_SPLITS = 10         /* num_splits outside 1..128                      */
+  FA_ERR_SPLITS = 10,        /* num_splits outside 1..128                      */
+  FA_ERR_HEADS = 11          /* H is not a multiple of Hkv                     */
 };
 
 /*
@@ -103,7 +104,9 @@ int fa_fwd_f32(const float* q, const float* k, const float* v, float* o,
  *               between calls, and calls sharing one workspace must not run
  *               concurrently).
  * Errors as for fa_fwd, plus FA_ERR_SHAPE for causal with Nq > Nk,
- * FA_ERR_SPLITS and FA_ERR_WORKSPACE.  Two kernels are queued on `stream`.
+ * FA_ERR_SPLITS and FA_ERR_WORKSPACE.  With num_splits > 1 two kernels are
+ * queued on `stream`; with num_splits == 1 the single-pass kernel writes O
+ * and LSE directly (the workspace is still required and left untouched).
  */
 int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
                    int B, int H, int Nq, int Nk, int d, float scale, int causal,
@@ -118,6 +121,38 @@ size_t fa_fwd_splitkv_workspace_size(int B, int H, int Nq, int d, int num_splits
  * num_cus compute units (<= 0 means 256), keeping chunks of at least four
  * 64-key tiles.  Host only, no HIP call. */
 int fa_fwd_splitkv_num_splits(int B, int H, int Nq, int Nk, int num_cus);
+
+/*
+ * Attention forward with grouped K/V heads (bf16): multi-query and
+ * grouped-query attention, the variants that cut K/V reads (aiqz.cc Flash
+ * Attention IO article, section 性能调优经验).  Query head h of batch b reads
+ * K/V head h / (H / Hkv) of batch b; Hkv == H is ordinary multi-head
+ * attention, Hkv == 1 multi-query attention.
+ *   q, o      : [B,H,Nq,d] bf16;  k, v : [B,Hkv,Nk,d] bf16;  lse : [B,H,Nq] fp32.
+ *   H, Hkv    : query heads and K/V heads, Hkv >= 1 dividing H.
+ *   Nq, Nk    : query rows and keys per head, >= 1; causal aligns the last
+ *               query with the last key (query i sees keys j <= i + Nk - Nq)
+ *               and needs Nq <= Nk.  The H/Hkv query heads of a K/V head
+ *               must hold fewer than 2^31 rows together.
+ *   num_splits: 1 -> one pass, O and LSE written directly, workspace ignored
+ *               (may be NULL); 2..128 -> the keys are cut into chunks merged
+ *               as in fa_fwd_splitkv, with a workspace of at least
+ *               fa_fwd_splitkv_workspace_size(B, H, Nq, d, num_splits) bytes
+ *               (the partials are per query row).
+ * The query heads sharing a K/V head are processed together: short query
+ * blocks (decoding) are packed into one tile, so K/V is read once per K/V
+ * head rather than once per query head.  Results equal those of fa_fwd_splitkv
+ * on K/V with every head repeated H/Hkv times, up to rounding order.
+ * Errors as for fa_fwd_splitkv, plus FA_ERR_HEADS.
+ */
+int fa_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse,
+               int B, int H, int Hkv, int Nq, int Nk, int d, float scale, int causal,
+               int num_splits, void* workspace, size_t workspace_bytes,
+               hipStream_t stream);
+
+/* A chunk count for fa_fwd_gqa, chosen as fa_fwd_splitkv_num_splits does
+ * (1 if an argument is out of range).  Host only, no HIP call. */
+int fa_fwd_gqa_num_splits(int B, int H, int Hkv, int Nq, int Nk, int causal, int num_cus);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* fa_strerror(int status);

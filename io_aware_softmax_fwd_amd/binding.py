@@ -11,11 +11,16 @@ Low level (same names and arguments as the C functions, raw pointers):
                    num_splits, workspace, workspace_bytes, stream) -> status
     fa_fwd_splitkv_workspace_size(B, H, Nq, d, num_splits)     -> bytes
     fa_fwd_splitkv_num_splits(B, H, Nq, Nk, num_cus)           -> count
+    fa_fwd_gqa(q, k, v, o, lse, B, H, Hkv, Nq, Nk, d, scale, causal,
+               num_splits, workspace, workspace_bytes, stream) -> status
+    fa_fwd_gqa_num_splits(B, H, Hkv, Nq, Nk, causal, num_cus)  -> count
     fa_strerror(status)                                        -> str
 High level (torch tensors on a ROCm device):
     fwd(q, k, v, scale=None, causal=False, out=None, lse=None) -> (o, lse)
     fwd_splitkv(q, k, v, scale=None, causal=False, num_splits=None,
                 workspace=None)                                -> (o, lse)
+    fwd_gqa(q, k, v, scale=None, causal=False, num_splits=1,
+            workspace=None)                                    -> (o, lse)
 """
 import ctypes
 import math
@@ -34,9 +39,10 @@ FA_ERR_CAUSAL = 7
 FA_ERR_ALIAS = 8
 FA_ERR_WORKSPACE = 9
 FA_ERR_SPLITS = 10
+FA_ERR_HEADS = 11
 
 EXPORTED = ("fa_fwd", "fa_fwd_f32", "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_size",
-            "fa_fwd_splitkv_num_splits", "fa_strerror")
+            "fa_fwd_splitkv_num_splits", "fa_fwd_gqa", "fa_fwd_gqa_num_splits", "fa_strerror")
 
 _lib = None
 
@@ -70,6 +76,12 @@ def load():
     lib.fa_fwd_splitkv_workspace_size.argtypes = [ctypes.c_int] * 5
     lib.fa_fwd_splitkv_num_splits.restype = ctypes.c_int
     lib.fa_fwd_splitkv_num_splits.argtypes = [ctypes.c_int] * 5
+    lib.fa_fwd_gqa.restype = ctypes.c_int
+    lib.fa_fwd_gqa.argtypes = ([ctypes.c_void_p] * 5 + [ctypes.c_int] * 6 +
+                               [ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                ctypes.c_size_t, ctypes.c_void_p])
+    lib.fa_fwd_gqa_num_splits.restype = ctypes.c_int
+    lib.fa_fwd_gqa_num_splits.argtypes = [ctypes.c_int] * 7
     lib.fa_strerror.restype = ctypes.c_char_p
     lib.fa_strerror.argtypes = [ctypes.c_int]
     _lib = lib
@@ -96,6 +108,16 @@ def fa_fwd_splitkv_workspace_size(B, H, Nq, d, num_splits):
 
 def fa_fwd_splitkv_num_splits(B, H, Nq, Nk, num_cus):
     return int(load().fa_fwd_splitkv_num_splits(B, H, Nq, Nk, num_cus))
+
+
+def fa_fwd_gqa(q, k, v, o, lse, B, H, Hkv, Nq, Nk, d, scale, causal, num_splits, workspace,
+               workspace_bytes, stream):
+    return load().fa_fwd_gqa(q, k, v, o, lse, B, H, Hkv, Nq, Nk, d, scale, causal, num_splits,
+                             workspace, workspace_bytes, stream)
+
+
+def fa_fwd_gqa_num_splits(B, H, Hkv, Nq, Nk, causal, num_cus):
+    return int(load().fa_fwd_gqa_num_splits(B, H, Hkv, Nq, Nk, causal, num_cus))
 
 
 def fa_strerror(status):
@@ -181,4 +203,48 @@ def fwd_splitkv(q, k, v, scale=None, causal=False, num_splits=None, workspace=No
                         workspace.data_ptr(), workspace.numel() * workspace.element_size(), stream)
     if st != FA_OK:
         raise FaError(st, "fa_fwd_splitkv")
+    return out, lse
+
+
+def fwd_gqa(q, k, v, scale=None, causal=False, num_splits=1, workspace=None,
+            out=None, lse=None, stream=None):
+    """Grouped-K/V-head attention forward of bf16 torch tensors: q [B,H,Nq,d],
+    k and v [B,Hkv,Nk,d] with Hkv dividing H (contiguous, on the GPU).
+    num_splits=None takes the library's suggestion for this GPU; with more
+    than one split a workspace (uint8 device tensor) is allocated here if not
+    given.  Returns (o, lse)."""
+    import torch
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor):
+            raise TypeError("%s must be a torch.Tensor" % name)
+        if t.device.type != "cuda" or not t.is_contiguous() or t.dim() != 4:
+            raise ValueError("%s must be a contiguous 4-D GPU tensor" % name)
+        if t.dtype != torch.bfloat16:
+            raise TypeError("%s must be bfloat16" % name)
+    B, H, Nq, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    if k.shape != (B, Hkv, Nk, d) or v.shape != k.shape:
+        raise ValueError("k and v must be [B, Hkv, Nk, d] with q's B and d")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if num_splits is None:
+        cus = torch.cuda.get_device_properties(q.device).multi_processor_count
+        num_splits = fa_fwd_gqa_num_splits(B, H, Hkv, Nq, Nk, int(bool(causal)), cus)
+    ws_ptr, ws_bytes = None, 0
+    if num_splits > 1:
+        if workspace is None:
+            need = fa_fwd_splitkv_workspace_size(B, H, Nq, d, num_splits)
+            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    st = fa_fwd_gqa(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                    B, H, Hkv, Nq, Nk, d, float(scale), int(bool(causal)), int(num_splits),
+                    ws_ptr, ws_bytes, stream)
+    if st != FA_OK:
+        raise FaError(st, "fa_fwd_gqa")
     return out, lse

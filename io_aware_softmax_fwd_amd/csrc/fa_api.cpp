@@ -47,36 +47,57 @@ int validate(const void* q, const void* k, const void* v, const void* o, const f
   return FA_OK;
 }
 
-int validate_split(const void* q, const void* k, const void* v, const void* o, const float* lse,
-                   int B, int H, int Nq, int Nk, int d, float scale, int causal, int splits,
-                   const void* ws, size_t ws_bytes) {
+// Checks of the general bf16 call (grouped K/V heads, Nq != Nk, key
+// splits).  A workspace is required only when splits > 1.
+int validate_gqa(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                 int B, int H, int Hkv, int Nq, int Nk, int d, float scale, int causal, int splits,
+                 const void* ws, size_t ws_bytes) {
   if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
-  if (B < 1 || H < 1 || Nq < 1 || Nk < 1) return FA_ERR_SHAPE;
+  if (B < 1 || H < 1 || Hkv < 1 || Nq < 1 || Nk < 1) return FA_ERR_SHAPE;
+  if (H % Hkv != 0) return FA_ERR_HEADS;
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED_D;
-  const int64_t qrows = (int64_t)B * H * Nq, krows = (int64_t)B * H * Nk;
+  const int64_t qrows = (int64_t)B * H * Nq, krows = (int64_t)B * Hkv * Nk;
   if (qrows * d >= kMaxElems || krows * d >= kMaxElems) return FA_ERR_SHAPE;
-  if ((int64_t)Nk * d * 2 >= (int64_t(1) << 31) || (int64_t)Nq * d * 2 >= (int64_t(1) << 31))
+  // One K/V head below 2 GiB (32-bit byte offsets inside a head) and the
+  // query rows of one K/V head below 2^31.
+  if ((int64_t)Nk * d * 2 >= (int64_t(1) << 31) || (int64_t)Nq * d * 2 >= (int64_t(1) << 31) ||
+      (int64_t)(H / Hkv) * Nq >= (int64_t(1) << 31))
     return FA_ERR_SHAPE;
   if (!(scale > 0.f) || !isfinite(scale)) return FA_ERR_SCALE;
   if (causal != 0 && causal != 1) return FA_ERR_CAUSAL;
   if (causal && Nq > Nk) return FA_ERR_SHAPE;
   if (splits < 1 || splits > kMaxSplits) return FA_ERR_SPLITS;
-  const int64_t n_qtiles = (Nq + 127) / 128;
-  if (n_qtiles * splits * B * H >= (int64_t(1) << 31)) return FA_ERR_SHAPE;
+  const fa::QueryTiling t = fa::query_tiling(H / Hkv, Nq, causal);
+  if (t.n_qtiles * splits * B * Hkv >= (int64_t(1) << 31)) return FA_ERR_SHAPE;
+  // the merge's 1-D grid: one thread per (query row, 8 head dims)
+  if (splits > 1 && qrows * (d / 8) >= (int64_t(1) << 31)) return FA_ERR_SHAPE;
   if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(o) || misaligned(lse))
     return FA_ERR_ALIGN;
-  const fa::SplitLayout L = fa::splitkv_layout(B, H, Nq, d, splits);
-  if (!ws || (int64_t)ws_bytes < L.total) return FA_ERR_WORKSPACE;
-  if (misaligned(ws)) return FA_ERR_ALIGN;
   const int64_t qb = qrows * d * 2, kb = krows * d * 2, lb = qrows * 4;
   if (overlap(o, qb, q, qb) || overlap(o, qb, k, kb) || overlap(o, qb, v, kb) ||
       overlap(lse, lb, q, qb) || overlap(lse, lb, k, kb) || overlap(lse, lb, v, kb) ||
       overlap(lse, lb, o, qb))
     return FA_ERR_ALIAS;
-  if (overlap(ws, L.total, q, qb) || overlap(ws, L.total, k, kb) || overlap(ws, L.total, v, kb) ||
-      overlap(ws, L.total, o, qb) || overlap(ws, L.total, lse, lb))
-    return FA_ERR_ALIAS;
+  if (splits > 1) {
+    const fa::SplitLayout L = fa::splitkv_layout(B, H, Nq, d, splits);
+    if (!ws || (int64_t)ws_bytes < L.total) return FA_ERR_WORKSPACE;
+    if (misaligned(ws)) return FA_ERR_ALIGN;
+    if (overlap(ws, L.total, q, qb) || overlap(ws, L.total, k, kb) || overlap(ws, L.total, v, kb) ||
+        overlap(ws, L.total, o, qb) || overlap(ws, L.total, lse, lb))
+      return FA_ERR_ALIAS;
+  }
   return FA_OK;
+}
+
+// About four workgroups per CU (two resident, two queued), keeping at least
+// four 64-key tiles per chunk.
+int choose_splits(int B, int H, int Hkv, int Nq, int Nk, int causal, int num_cus) {
+  if (B < 1 || H < 1 || Hkv < 1 || H % Hkv != 0 || Nq < 1 || Nk < 1) return 1;
+  if (num_cus < 1) num_cus = 256;
+  const int64_t base = fa::query_tiling(H / Hkv, Nq, causal != 0).n_qtiles * B * Hkv;
+  const int64_t want = ((int64_t)4 * num_cus + base - 1) / base;
+  const int64_t most = std::max<int64_t>(1, ((Nk + 63) / 64) / 4);
+  return (int)std::max<int64_t>(1, std::min<int64_t>(std::min<int64_t>(want, most), kMaxSplits));
 }
 
 }  // namespace
@@ -87,7 +108,7 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
            int d, float scale, int causal, hipStream_t stream) {
   const int st = validate(q, k, v, o, lse, B, H, N, d, scale, causal, 2);
   if (st != FA_OK) return st;
-  const fa::Problem p{q, k, v, o, lse, B, H, N, d, scale, causal};
+  const fa::GqaProblem p{q, k, v, o, lse, B, H, H, N, N, d, scale, causal, 1, nullptr};
   return fa::launch_fwd_bf16(p, stream) == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
@@ -106,24 +127,38 @@ size_t fa_fwd_splitkv_workspace_size(int B, int H, int Nq, int d, int num_splits
 }
 
 int fa_fwd_splitkv_num_splits(int B, int H, int Nq, int Nk, int num_cus) {
-  if (B < 1 || H < 1 || Nq < 1 || Nk < 1) return 1;
-  if (num_cus < 1) num_cus = 256;
-  // Aim for four workgroups per CU (two resident, two queued) while keeping
-  // at least four 64-key tiles per chunk.
-  const int64_t base = (int64_t)((Nq + 127) / 128) * B * H;
-  const int64_t want = ((int64_t)4 * num_cus + base - 1) / base;
-  const int64_t most = std::max<int64_t>(1, ((Nk + 63) / 64) / 4);
-  return (int)std::max<int64_t>(1, std::min<int64_t>(std::min<int64_t>(want, most), kMaxSplits));
+  // causal and non-causal calls cut a head's queries into the same tiles
+  // when every K/V head serves one query head
+  return choose_splits(B, H, H, Nq, Nk, 0, num_cus);
 }
 
 int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
                    int Nq, int Nk, int d, float scale, int causal, int num_splits, void* workspace,
                    size_t workspace_bytes, hipStream_t stream) {
-  const int st = validate_split(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, num_splits,
-                                workspace, workspace_bytes);
+  const int st = validate_gqa(q, k, v, o, lse, B, H, H, Nq, Nk, d, scale, causal, num_splits,
+                              workspace, workspace_bytes);
   if (st != FA_OK) return st;
-  const fa::SplitProblem p{q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, num_splits, workspace};
-  return fa::launch_fwd_bf16_splitkv(p, stream) == hipSuccess ? FA_OK : FA_ERR_HIP;
+  // the workspace is part of this entry point's contract even for one split
+  if (!workspace || workspace_bytes < fa_fwd_splitkv_workspace_size(B, H, Nq, d, num_splits))
+    return FA_ERR_WORKSPACE;
+  if (misaligned(workspace)) return FA_ERR_ALIGN;
+  const fa::GqaProblem p{q, k, v, o, lse, B, H, H, Nq, Nk, d, scale, causal, num_splits, workspace};
+  return fa::launch_fwd_bf16(p, stream) == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+int fa_fwd_gqa_num_splits(int B, int H, int Hkv, int Nq, int Nk, int causal, int num_cus) {
+  return choose_splits(B, H, Hkv, Nq, Nk, causal, num_cus);
+}
+
+int fa_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+               int Hkv, int Nq, int Nk, int d, float scale, int causal, int num_splits,
+               void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  const int st = validate_gqa(q, k, v, o, lse, B, H, Hkv, Nq, Nk, d, scale, causal, num_splits,
+                              workspace, workspace_bytes);
+  if (st != FA_OK) return st;
+  const fa::GqaProblem p{q, k, v, o, lse, B, H, Hkv, Nq, Nk, d, scale, causal, num_splits,
+                         num_splits > 1 ? workspace : nullptr};
+  return fa::launch_fwd_bf16(p, stream) == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
 const char* fa_strerror(int status) {
@@ -139,6 +174,7 @@ const char* fa_strerror(int status) {
     case FA_ERR_ALIAS: return "an output or the workspace overlaps another buffer";
     case FA_ERR_WORKSPACE: return "workspace missing or smaller than the size query returns";
     case FA_ERR_SPLITS: return "num_splits must be between 1 and 128";
+    case FA_ERR_HEADS: return "H must be a multiple of Hkv";
     default: return "unknown status";
   }
 }

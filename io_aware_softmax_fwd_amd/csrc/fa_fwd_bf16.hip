@@ -36,6 +36,13 @@
 // for any offset; zzszmyf.github.io notes, section 5.1).
 // Causal: key tiles wholly above the diagonal are never loaded, masking is
 // applied only on diagonal tiles and on the ragged last tile.
+// Grouped K/V heads (MQA/GQA, the K/V-read saving named in the aiqz.cc
+// article's tuning section): the G query heads that share one K/V head are
+// adjacent in [B, H, Nq, d], so a K/V head's queries form one contiguous
+// block of G*Nq rows; row r of it sits at position r % Nq of its head.  A
+// workgroup's 128 rows are taken from that block, either one head at a time
+// (long causal heads, so the heaviest tiles can go first) or packed across
+// heads (short or non-causal heads: decoding with G heads reads K/V once).
 #include <math.h>
 
 #include "fa_internal.h"
@@ -121,9 +128,10 @@ struct Fwd {
   const unsigned short* kh;
   const unsigned short* vh;
   int N;                  // keys (Nk)
-  int Nq;                 // query rows
   int coff;               // causal offset Nk - Nq: query i sees keys j <= i + coff
-  int wave, l32, hl, qw;
+  int wave, l32, hl;
+  int pos[QB];            // position inside its head of this lane's query, per block
+  int wlast;              // causal: last key any valid query of this wave sees (-1: none)
   float c, thr;
   bf16x8 qf[QB][KS];      // Q fragments (B operand of S^T = K Q^T), per 32-row block
   f32x16 acc[QB][DB];     // O^T accumulators: lane holds query l%32 of each block
@@ -137,8 +145,6 @@ struct Fwd {
   // touch the buffers being read and inserts no wait for them.
   unsigned char* kbuf[2];
   unsigned char* vbuf[2];
-
-  __device__ int qi(int qb) const { return qw + 32 * qb + l32; }
 
   __device__ void setup_offsets(int lane) {
 #pragma unroll
@@ -180,7 +186,7 @@ struct Fwd {
   __device__ void softmax(int qb, f32x16 (&s)[KB], bf16x8 (&pf)[PS], int k0) {
     if constexpr (MASK) {
       // key = k0 + 32*kb + (r&3) + 8*(r>>2) + 4*hl must be <= min(qi+coff, N-1)
-      const int lim = (CAUSAL ? min(qi(qb) + coff, N - 1) : N - 1) - k0 - 4 * hl;
+      const int lim = (CAUSAL ? min(pos[qb] + coff, N - 1) : N - 1) - k0 - 4 * hl;
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
@@ -293,21 +299,39 @@ struct Fwd {
     }
     // Causal: a wave whose last query precedes the tile's first key has
     // nothing to do here or later; the barrier below stays unconditional.
-    if (!MASK || !CAUSAL || k0 <= qw + WR - 1 + coff) consume<MASK, PAR>(k0);
+    if (!MASK || !CAUSAL || k0 <= wlast) consume<MASK, PAR>(k0);
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
     __builtin_amdgcn_s_barrier();
   }
 };
 
-// One workgroup per (query tile, key chunk, batch*head).  Without SPLIT the
-// single chunk is every key and O/LSE are written directly; with SPLIT the
-// chunk's own normalised O (fp32) and LSE go to opart/lpart for the merge.
+// Positions covered by rows [a, a + n) (n >= 1) of a K/V head's query block
+// (row r is position r % Nq): one run when the rows stay inside one head,
+// else every position of a head.
+__device__ __forceinline__ void position_range(int a, int n, int Nq, int& lo, int& hi) {
+  const int p0 = a % Nq;
+  if (p0 + n - 1 < Nq) {
+    lo = p0;
+    hi = p0 + n - 1;
+  } else {
+    lo = 0;
+    hi = Nq - 1;
+  }
+}
+
+// One workgroup per (query tile, key chunk, batch * K/V head).  The query
+// rows of K/V head bkv are rows [bkv*G*Nq, (bkv+1)*G*Nq) of Q, O and LSE.
+// tph > 0: tiles stay inside one query head (tph tiles per head, G heads);
+// tph == 0: tiles are packed over the whole block of G*Nq rows.  Without
+// SPLIT the single chunk is every key and O/LSE are written directly; with
+// SPLIT the chunk's own normalised O (fp32) and LSE go to opart/lpart for
+// the merge.
 template <int D, int QB, bool CAUSAL, bool SPLIT>
 __global__ __launch_bounds__(kThreads, QB == 1 ? 2 : 1) void fwd_bf16_kernel(
     const unsigned short* __restrict__ q, const unsigned short* __restrict__ k,
     const unsigned short* __restrict__ v, unsigned short* __restrict__ o,
-    float* __restrict__ lse, int Nq, int Nk, int BH, int n_qtiles, float scale, int splits,
-    float* __restrict__ opart, float* __restrict__ lpart) {
+    float* __restrict__ lse, int Nq, int Nk, int G, int BHkv, int n_qtiles, int tph,
+    float scale, int splits, float* __restrict__ opart, float* __restrict__ lpart) {
   __shared__ __attribute__((aligned(1024))) unsigned char k_lds0[Cfg<D>::kTile];
   __shared__ __attribute__((aligned(1024))) unsigned char k_lds1[Cfg<D>::kTile];
   __shared__ __attribute__((aligned(1024))) unsigned char v_lds0[Cfg<D>::vTile];
@@ -318,16 +342,25 @@ __global__ __launch_bounds__(kThreads, QB == 1 ? 2 : 1) void fwd_bf16_kernel(
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  // Heaviest query tiles first (causal work grows with the tile index); heads
-  // vary fastest, so with B*H a multiple of 8 every tile of a head lands on
-  // the same XCD and shares its L2.
-  const int bh = blockIdx.x % BH;
-  const int rest = blockIdx.x / BH;
+  // Heaviest query tiles first (causal work grows with the position); K/V
+  // heads vary fastest, so with B*Hkv a multiple of 8 every tile reading one
+  // K/V head lands on the same XCD and shares its L2.
+  const int bkv = blockIdx.x % BHkv;
+  const int rest = blockIdx.x / BHkv;
   const int split = SPLIT ? rest % splits : 0;
-  const int qt = n_qtiles - 1 - (SPLIT ? rest / splits : rest);
-  const int q0 = qt * BR;
-  const int64_t qhead = (int64_t)bh * Nq * D;
-  const int64_t khead = (int64_t)bh * Nk * D;
+  const int idx = SPLIT ? rest / splits : rest;
+  const int R = G * Nq;                  // query rows per K/V head
+  int r0, nr;                            // this tile: rows [r0, r0 + nr) of the block
+  if (tph == 0) {
+    r0 = (n_qtiles - 1 - idx) * BR;
+    nr = min(BR, R - r0);
+  } else {
+    const int pt = tph - 1 - idx / G;
+    r0 = (idx % G) * Nq + pt * BR;
+    nr = min(BR, Nq - pt * BR);
+  }
+  const int64_t qblock = (int64_t)bkv * R;   // first Q/O/LSE row of the block
+  const int64_t khead = (int64_t)bkv * Nk * D;
 
   F f;
   f.kbuf[0] = k_lds0;
@@ -337,12 +370,20 @@ __global__ __launch_bounds__(kThreads, QB == 1 ? 2 : 1) void fwd_bf16_kernel(
   f.kh = k + khead;
   f.vh = v + khead;
   f.N = Nk;
-  f.Nq = Nq;
   f.coff = Nk - Nq;
   f.wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   f.l32 = lane & 31;
   f.hl = lane >> 5;
-  f.qw = q0 + f.wave * F::WR;
+  {
+    const int w0 = f.wave * F::WR;       // first row of this wave in the tile
+    int lo, hi;
+    if (w0 < nr) {
+      position_range(r0 + w0, min(F::WR, nr - w0), Nq, lo, hi);
+      f.wlast = hi + f.coff;
+    } else {
+      f.wlast = -1;
+    }
+  }
   f.c = scale * kLog2e;
   f.thr = kLazy / f.c;
 #pragma unroll
@@ -353,24 +394,28 @@ __global__ __launch_bounds__(kThreads, QB == 1 ? 2 : 1) void fwd_bf16_kernel(
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int r = 0; r < 16; ++r) f.acc[qb][db][r] = 0.f;
-    const int qi = f.qi(qb);
+    const int lr = f.wave * F::WR + 32 * qb + f.l32;   // row inside the tile
+    f.pos[qb] = (r0 + lr) % Nq;
+    const unsigned short* qrow = q + (qblock + r0 + lr) * D;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       u32x4 raw = {0u, 0u, 0u, 0u};
-      if (qi < Nq) raw = *reinterpret_cast<const u32x4*>(q + qhead + (int64_t)qi * D + 16 * ks + 8 * f.hl);
+      if (lr < nr) raw = *reinterpret_cast<const u32x4*>(qrow + 16 * ks + 8 * f.hl);
       f.qf[qb][ks] = __builtin_bit_cast(bf16x8, raw);
     }
   }
   f.setup_offsets(lane);
 
   // Key tiles this workgroup's rows need, and its chunk [t0, t1) of them.
-  const int kv_end = CAUSAL ? min(Nk, q0 + BR + f.coff) : Nk;
+  int pmin, pmax;
+  position_range(r0, nr, Nq, pmin, pmax);
+  const int kv_end = CAUSAL ? min(Nk, pmax + 1 + f.coff) : Nk;
   const int n_tiles = (kv_end + kKeys - 1) / kKeys;
   const int t0 = SPLIT ? (int)((int64_t)split * n_tiles / splits) : 0;
   const int t1 = SPLIT ? (int)((int64_t)(split + 1) * n_tiles / splits) : n_tiles;
   // Tiles before n_full need no mask: every key is < Nk and, when causal,
-  // visible to the workgroup's first query.
-  const int n_full = CAUSAL ? min(q0 + f.coff + 1, Nk) / kKeys : Nk / kKeys;
+  // visible to the workgroup's earliest query.
+  const int n_full = CAUSAL ? min(pmin + f.coff + 1, Nk) / kKeys : Nk / kKeys;
 
   if (t0 < t1) {
     f.template issue<false, 0>(t0 * kKeys);
@@ -397,13 +442,13 @@ __global__ __launch_bounds__(kThreads, QB == 1 ? 2 : 1) void fwd_bf16_kernel(
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const float l_tot = sum_across_halves(f.l[qb]);
-    const int qi = f.qi(qb);
-    if (qi >= Nq) continue;
-    const int64_t row = (int64_t)bh * Nq + qi;
+    const int lr = f.wave * F::WR + 32 * qb + f.l32;
+    if (lr >= nr) continue;
+    const int64_t row = qblock + r0 + lr;
     if constexpr (!SPLIT) {
       // O = acc / l in bf16 (round to nearest even), LSE = scale*m + ln l.
       const float inv = 1.f / l_tot;
-      unsigned short* orow = o + qhead + (int64_t)qi * D;
+      unsigned short* orow = o + row * D;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -419,7 +464,7 @@ __global__ __launch_bounds__(kThreads, QB == 1 ? 2 : 1) void fwd_bf16_kernel(
       // chunk gets O = 0 and LSE = -inf (weight 0 in the merge)
       const bool empty = !(l_tot > 0.f);
       const float inv = empty ? 0.f : 1.f / l_tot;
-      const int64_t prow = (int64_t)split * BH * Nq + row;
+      const int64_t prow = (int64_t)split * BHkv * R + row;
       float* orow = opart + prow * D;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
@@ -437,14 +482,99 @@ __global__ __launch_bounds__(kThreads, QB == 1 ? 2 : 1) void fwd_bf16_kernel(
 
 // Merge of the key chunks of every row: LSE = log sum_s exp(LSE_s) and
 // O = sum_s exp(LSE_s - LSE) O_s, the online-softmax merge applied to whole
-// chunks (zzszmyf.github.io notes, sections 5 and 12.1).  One thread per
-// (row, 8 head dims); chunk 0 always holds key 0, so the max is finite.
+// chunks (zzszmyf.github.io notes, sections 5 and 12.1).  One workgroup per
+// row, so the chunks are read in parallel rather than one memory latency
+// after another: the max and the weight sum over chunks are block
+// reductions, then wave w adds chunks w, w+4, ... over all head dims and
+// the four partial sums meet in LDS.  Chunk 0 always holds key 0, so the
+// max is finite.
+constexpr int kMergeThreads = 256;
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) x = fmaxf(x, __shfl_xor(x, off, 64));
+  return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
+  return x;
+}
+
 template <int D>
-__global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ opart,
-                                                    const float* __restrict__ lpart,
-                                                    unsigned short* __restrict__ o,
-                                                    float* __restrict__ lse, int64_t rows,
-                                                    int splits) {
+__global__ __launch_bounds__(kMergeThreads) void merge_kernel(const float* __restrict__ opart,
+                                                              const float* __restrict__ lpart,
+                                                              unsigned short* __restrict__ o,
+                                                              float* __restrict__ lse,
+                                                              int64_t rows, int splits) {
+  constexpr int NW = kMergeThreads / 64, PER = D / 64;   // dims per lane
+  __shared__ float red[NW];
+  __shared__ float part[NW][D];
+  const int64_t row = blockIdx.x;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+
+  float mx = -INFINITY;
+  for (int sp = tid; sp < splits; sp += kMergeThreads) mx = fmaxf(mx, lpart[(int64_t)sp * rows + row]);
+  mx = wave_max(mx);
+  if (lane == 0) red[wave] = mx;
+  __syncthreads();
+  mx = red[0];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) mx = fmaxf(mx, red[w]);
+  __syncthreads();
+
+  float sum = 0.f;
+  float acc[PER];
+#pragma unroll
+  for (int e = 0; e < PER; ++e) acc[e] = 0.f;
+#pragma unroll 4
+  for (int sp = wave; sp < splits; sp += NW) {
+    const float ls = lpart[(int64_t)sp * rows + row];
+    const float w = ls == -INFINITY ? 0.f : expf(ls - mx);
+    sum += w;
+    const float* src = opart + ((int64_t)sp * rows + row) * D + PER * lane;
+    if constexpr (PER == 2) {
+      const float2 a = *reinterpret_cast<const float2*>(src);
+      acc[0] += w * a.x;
+      acc[1] += w * a.y;
+    } else {
+      acc[0] += w * src[0];
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < PER; ++e) part[wave][PER * lane + e] = acc[e];
+  if (lane == 0) red[wave] = sum;     // every lane of a wave holds the same sum
+  __syncthreads();
+  if (wave != 0) return;
+  float tot = red[0];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) tot += red[w];
+  const float inv = 1.f / tot;
+  float r[PER];
+#pragma unroll
+  for (int e = 0; e < PER; ++e) {
+    float t = part[0][PER * lane + e];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) t += part[w][PER * lane + e];
+    r[e] = t * inv;
+  }
+  if constexpr (PER == 2) {
+    *reinterpret_cast<unsigned*>(o + row * D + 2 * lane) = pack_bf16x2(r[0], r[1]);
+  } else {
+    o[row * D + lane] = (unsigned short)(pack_bf16x2(r[0], 0.f) & 0xffffu);
+  }
+  if (lane == 0) lse[row] = mx + logf(tot);
+}
+
+// The same merge for many rows: one thread per (row, 8 head dims), each
+// walking the chunks itself; enough threads to fill the GPU, where one
+// workgroup per row would spend most of its lanes on bookkeeping.
+template <int D>
+__global__ __launch_bounds__(256) void merge_rows_kernel(const float* __restrict__ opart,
+                                                         const float* __restrict__ lpart,
+                                                         unsigned short* __restrict__ o,
+                                                         float* __restrict__ lse, int64_t rows,
+                                                         int splits) {
   const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t row = t / (D / 8);
   const int c8 = (int)(t % (D / 8));
@@ -469,60 +599,53 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ op
   if (c8 == 0) lse[row] = mx + logf(sum);
 }
 
-template <int D, int QB, bool CAUSAL>
-hipError_t launch(const Problem& p, hipStream_t stream) {
-  constexpr int BR = 32 * QB * kWaves;
-  const int n_qtiles = (p.N + BR - 1) / BR;
-  const int BH = p.B * p.H;
-  const dim3 grid((unsigned)((int64_t)n_qtiles * BH)), block(kThreads);
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, QB, CAUSAL, false>), grid, block, 0, stream,
-                     static_cast<const unsigned short*>(p.q), static_cast<const unsigned short*>(p.k),
-                     static_cast<const unsigned short*>(p.v), static_cast<unsigned short*>(p.o),
-                     p.lse, p.N, p.N, BH, n_qtiles, p.scale, 1, nullptr, nullptr);
-  return hipGetLastError();
-}
+// Rows above which the merge runs one thread per (row, 8 dims).
+constexpr int64_t kMergeRowsMin = 4096;
 
 template <int D, bool CAUSAL>
-hipError_t launch_split(const SplitProblem& p, hipStream_t stream) {
+hipError_t launch(const GqaProblem& p, hipStream_t stream) {
   constexpr int BR = 32 * kWaves;
-  const int n_qtiles = (p.Nq + BR - 1) / BR;
-  const int BH = p.B * p.H;
+  static_assert(BR == kTileRows, "host tiling and kernel tile height differ");
+  const QueryTiling t = query_tiling(p.H / p.Hkv, p.Nq, p.causal);
+  const int BHkv = p.B * p.Hkv;
+  const int G = p.H / p.Hkv;
+  const dim3 block(kThreads);
+  const unsigned short* q = static_cast<const unsigned short*>(p.q);
+  const unsigned short* k = static_cast<const unsigned short*>(p.k);
+  const unsigned short* v = static_cast<const unsigned short*>(p.v);
+  if (p.splits == 1) {
+    const dim3 grid((unsigned)(t.n_qtiles * BHkv));
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, 1, CAUSAL, false>), grid, block, 0, stream, q, k, v,
+                       static_cast<unsigned short*>(p.o), p.lse, p.Nq, p.Nk, G, BHkv,
+                       (int)t.n_qtiles, t.tph, p.scale, 1, nullptr, nullptr);
+    return hipGetLastError();
+  }
   const SplitLayout L = splitkv_layout(p.B, p.H, p.Nq, p.d, p.splits);
   float* opart = static_cast<float*>(p.workspace);
   float* lpart = reinterpret_cast<float*>(static_cast<unsigned char*>(p.workspace) + L.lse_offset);
-  const dim3 grid((unsigned)((int64_t)n_qtiles * p.splits * BH)), block(kThreads);
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, 1, CAUSAL, true>), grid, block, 0, stream,
-                     static_cast<const unsigned short*>(p.q), static_cast<const unsigned short*>(p.k),
-                     static_cast<const unsigned short*>(p.v), nullptr, nullptr, p.Nq, p.Nk, BH,
-                     n_qtiles, p.scale, p.splits, opart, lpart);
+  const dim3 grid((unsigned)(t.n_qtiles * p.splits * BHkv));
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, 1, CAUSAL, true>), grid, block, 0, stream, q, k, v,
+                     nullptr, nullptr, p.Nq, p.Nk, G, BHkv, (int)t.n_qtiles, t.tph, p.scale,
+                     p.splits, opart, lpart);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int64_t rows = (int64_t)BH * p.Nq;
-  const int64_t threads = rows * (D / 8);
-  const dim3 mgrid((unsigned)((threads + 255) / 256)), mblock(256);
-  hipLaunchKernelGGL((merge_kernel<D>), mgrid, mblock, 0, stream, opart, lpart,
-                     static_cast<unsigned short*>(p.o), p.lse, rows, p.splits);
+  const int64_t rows = (int64_t)p.B * p.H * p.Nq;
+  if (rows >= kMergeRowsMin) {
+    const int64_t threads = rows * (D / 8);
+    hipLaunchKernelGGL((merge_rows_kernel<D>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
+                       stream, opart, lpart, static_cast<unsigned short*>(p.o), p.lse, rows, p.splits);
+  } else {
+    hipLaunchKernelGGL((merge_kernel<D>), dim3((unsigned)rows), dim3(kMergeThreads), 0, stream, opart,
+                       lpart, static_cast<unsigned short*>(p.o), p.lse, rows, p.splits);
+  }
   return hipGetLastError();
 }
 
 }  // namespace
 
-#ifndef FA_QB128
-#define FA_QB128 1
-#endif
-#ifndef FA_QB64
-#define FA_QB64 1
-#endif
-
-hipError_t launch_fwd_bf16(const Problem& p, hipStream_t stream) {
-  if (p.d == 64)
-    return p.causal ? launch<64, FA_QB64, true>(p, stream) : launch<64, FA_QB64, false>(p, stream);
-  return p.causal ? launch<128, FA_QB128, true>(p, stream) : launch<128, FA_QB128, false>(p, stream);
-}
-
-hipError_t launch_fwd_bf16_splitkv(const SplitProblem& p, hipStream_t stream) {
-  if (p.d == 64) return p.causal ? launch_split<64, true>(p, stream) : launch_split<64, false>(p, stream);
-  return p.causal ? launch_split<128, true>(p, stream) : launch_split<128, false>(p, stream);
+hipError_t launch_fwd_bf16(const GqaProblem& p, hipStream_t stream) {
+  if (p.d == 64) return p.causal ? launch<64, true>(p, stream) : launch<64, false>(p, stream);
+  return p.causal ? launch<128, true>(p, stream) : launch<128, false>(p, stream);
 }
 
 }  // namespace fa

@@ -18,21 +18,45 @@ struct Problem {
   int causal;
 };
 
-// Key-split problem: Nq query rows over Nk keys, the keys of every query
-// tile cut into `splits` chunks whose partial results go to `workspace`
-// (layout in splitkv_layout) before a merge writes o and lse.
-struct SplitProblem {
+// bf16 problem: B*H query heads of Nq rows over B*Hkv K/V heads of Nk keys
+// (query head h reads K/V head h / (H / Hkv)); with splits > 1 the keys of
+// every query tile are cut into `splits` chunks whose partial results go to
+// `workspace` (layout in splitkv_layout) before a merge writes o and lse.
+struct GqaProblem {
   const void* q;
   const void* k;
   const void* v;
   void* o;
   float* lse;
-  int B, H, Nq, Nk, d;
+  int B, H, Hkv, Nq, Nk, d;
   float scale;
   int causal;
   int splits;
   void* workspace;
 };
+
+// Query rows per workgroup tile of the bf16 kernel.
+constexpr int kTileRows = 128;
+
+// How the G*Nq query rows that share one K/V head are cut into tiles.
+// tph > 0: tph tiles per query head, never crossing heads (long causal heads:
+// tiles can be ordered heaviest first); tph == 0: tiles packed across the G
+// heads (all other cases; a decoding step of G heads then reads K/V once).
+struct QueryTiling {
+  int tph;
+  int64_t n_qtiles;   // tiles per K/V head
+};
+inline QueryTiling query_tiling(int G, int Nq, int causal) {
+  QueryTiling t;
+  if (causal && Nq >= kTileRows) {
+    t.tph = (Nq + kTileRows - 1) / kTileRows;
+    t.n_qtiles = (int64_t)G * t.tph;
+  } else {
+    t.tph = 0;
+    t.n_qtiles = ((int64_t)G * Nq + kTileRows - 1) / kTileRows;
+  }
+  return t;
+}
 
 // Workspace layout of the key-split path: partial outputs, fp32
 // [splits][B*H*Nq][d], then partial LSEs, fp32 [splits][B*H*Nq], each part
@@ -52,7 +76,6 @@ inline SplitLayout splitkv_layout(int B, int H, int Nq, int d, int splits) {
 // Each launcher queues its kernels on `stream` and returns the HIP status of
 // the launch (hipSuccess or the runtime's error).
 hipError_t launch_fwd_f32(const Problem& p, hipStream_t stream);
-hipError_t launch_fwd_bf16(const Problem& p, hipStream_t stream);
-hipError_t launch_fwd_bf16_splitkv(const SplitProblem& p, hipStream_t stream);
+hipError_t launch_fwd_bf16(const GqaProblem& p, hipStream_t stream);
 
 }  // namespace fa

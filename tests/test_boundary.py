@@ -74,12 +74,14 @@ def test_bad_arguments_rejected_on_host(fn, kw, status):
 
 
 def test_strerror_covers_every_status():
+    codes = [int(v) for _, v in re.findall(r"(FA_\w+)\s*=\s*(\d+)", open(HEADER).read())]
+    assert sorted(codes) == list(range(len(codes)))
     seen = set()
-    for s in range(9):
+    for s in codes:
         msg = fa.fa_strerror(s)
         assert msg and msg != "unknown status"
         seen.add(msg)
-    assert len(seen) == 9
+    assert len(seen) == len(codes)
     assert fa.fa_strerror(12345) == "unknown status"
 
 
@@ -128,3 +130,52 @@ def test_splitkv_workspace_size_and_split_choice():
     assert fa.fa_fwd_splitkv_num_splits(2, 8, 1024, 1024, 256) == 4
     assert fa.fa_fwd_splitkv_num_splits(1, 8, 1, 32768, 256) == 128
     assert fa.fa_fwd_splitkv_num_splits(1, 1, 1, 64, 256) == 1
+
+
+def _gqa_call(**kw):
+    args = dict(q=A, k=A + 8 * MB, v=A + 16 * MB, o=A + 24 * MB, lse=A + 32 * MB,
+                B=1, H=8, Hkv=2, Nq=16, Nk=128, d=64, scale=0.125, causal=0, splits=2,
+                ws=A + 64 * MB, ws_bytes=1 << 24, stream=None)
+    args.update(kw)
+    return fa.fa_fwd_gqa(args["q"], args["k"], args["v"], args["o"], args["lse"], args["B"],
+                         args["H"], args["Hkv"], args["Nq"], args["Nk"], args["d"], args["scale"],
+                         args["causal"], args["splits"], args["ws"], args["ws_bytes"],
+                         args["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), fa.FA_ERR_NULL), (dict(k=None), fa.FA_ERR_NULL),
+    (dict(Hkv=0), fa.FA_ERR_SHAPE), (dict(H=0), fa.FA_ERR_SHAPE),
+    (dict(Hkv=3), fa.FA_ERR_HEADS), (dict(H=8, Hkv=16), fa.FA_ERR_HEADS),
+    (dict(causal=1, Nq=129, Nk=128), fa.FA_ERR_SHAPE),
+    # the query rows of one K/V head must stay below 2^31
+    (dict(H=1 << 12, Hkv=1, Nq=1 << 19, Nk=1 << 19, splits=1), fa.FA_ERR_SHAPE),
+    (dict(d=32), fa.FA_ERR_UNSUPPORTED_D), (dict(scale=0.0), fa.FA_ERR_SCALE),
+    (dict(causal=2), fa.FA_ERR_CAUSAL),
+    (dict(splits=0), fa.FA_ERR_SPLITS), (dict(splits=200), fa.FA_ERR_SPLITS),
+    (dict(ws=None), fa.FA_ERR_WORKSPACE), (dict(ws_bytes=64), fa.FA_ERR_WORKSPACE),
+    (dict(ws=A + 64 * MB + 4), fa.FA_ERR_ALIGN), (dict(lse=A + 32 * MB + 8), fa.FA_ERR_ALIGN),
+    (dict(ws=A + 8 * MB), fa.FA_ERR_ALIAS), (dict(lse=A + 16 * MB), fa.FA_ERR_ALIAS),
+    # with one split the workspace is not used, so it is not checked; the
+    # error that remains is the alias of o with k
+    (dict(splits=1, ws=None, ws_bytes=0, o=A + 8 * MB), fa.FA_ERR_ALIAS),
+])
+def test_gqa_bad_arguments_rejected_on_host(kw, status):
+    assert _gqa_call(**kw) == status
+
+
+def test_gqa_split_choice():
+    # grouped heads of a decoding step share one tile per K/V head
+    assert fa.fa_fwd_gqa_num_splits(1, 32, 8, 1, 32768, 1, 256) == 128
+    assert fa.fa_fwd_gqa_num_splits(1, 32, 8, 1, 2048, 1, 256) == 8
+    # Hkv == H agrees with the multi-head choice
+    for args in ((2, 8, 1024, 1024), (1, 8, 1, 32768), (1, 32, 16384, 16384), (3, 5, 77, 900)):
+        B, H, Nq, Nk = args
+        for causal in (0, 1):
+            assert (fa.fa_fwd_gqa_num_splits(B, H, H, Nq, Nk, causal, 256)
+                    == fa.fa_fwd_splitkv_num_splits(B, H, Nq, Nk, 256))
+    # a long causal prefill over 8 K/V heads fills the GPU without a split
+    assert fa.fa_fwd_gqa_num_splits(1, 32, 8, 16384, 16384, 1, 256) == 1
+    # bad arguments give 1
+    assert fa.fa_fwd_gqa_num_splits(1, 6, 4, 1, 100, 0, 256) == 1
+    assert fa.fa_fwd_gqa_num_splits(0, 6, 3, 1, 100, 0, 256) == 1
