@@ -134,7 +134,14 @@ PROFILE_STEPS = {
            "SQ_ACTIVE_INST_LDS SQ_INSTS_VALU_TRANS_F32 SQ_ACTIVE_INST_ANY GRBM_GUI_ACTIVE "
            "--output-format csv -d $OUT/sq2 -o run "
            "-- python bench.py --steps 3 --warmup 1 --no-cpu-baseline",
+    "decode_gqa": "rocprofv3 --kernel-trace --stats --output-format csv -d $OUT/decode_gqa -o run "
+                  "-- python bench.py --decode 131072 --hkv 8",
+    "decode_mha": "rocprofv3 --kernel-trace --stats --output-format csv -d $OUT/decode_mha -o run "
+                  "-- python bench.py --decode 131072",
 }
+# extra kernel-trace steps summarised kernel by kernel: step -> summary name
+TRACE_ONLY = {"decode_gqa": "decode_b1_h32_hkv8_nk131072_d128",
+              "decode_mha": "decode_b1_h32_nk131072_d128"}
 KERNEL_KEY = "fwd_bf16_kernel"
 COPY_KEY = "copy"
 
@@ -212,6 +219,22 @@ def summarize(out_dir, workload_name):
             f.write("# rocprofv3 counters per launch, workload %s (kernel source %s)\n" % (workload_name, src_hash))
             f.write("# commands:\n#   %s\n#   %s\n" % (PROFILE_STEPS["sq"], PROFILE_STEPS["sq2"]))
             f.write("\n".join(sq_lines) + "\n")
+    # kernel-only traces of other calls (every kernel of the call)
+    for step, name in TRACE_ONLY.items():
+        st = glob.glob(os.path.join(out_dir, step, "**", "*kernel_stats.csv"), recursive=True)
+        if not st:
+            continue
+        out = []
+        with open(st[0]) as fh:
+            for row in csv.DictReader(fh):
+                if "fa" in row["Name"] and ("fwd_bf16_kernel" in row["Name"] or "merge" in row["Name"]):
+                    out.append("kernel: %s\ncalls=%s  average=%.2f us  min=%.2f us  max=%.2f us" % (
+                        row["Name"], row["Calls"], float(row["AverageNs"]) / 1e3,
+                        float(row["MinNs"]) / 1e3, float(row["MaxNs"]) / 1e3))
+        with open(os.path.join(prof, "fa_fwd_bf16_%s_kernel_trace.txt" % name), "w") as f:
+            f.write("# rocprofv3 kernel trace, %s (kernel source %s)\n" % (name, src_hash))
+            f.write("# command: %s\n" % PROFILE_STEPS[step])
+            f.write("\n".join(out) + "\n")
     print(json.dumps({"kernel_avg_us": avg_ns / 1e3 if avg_ns else None,
                       "traffic_bytes": rd + wr, "read": rd, "write": wr}))
 
