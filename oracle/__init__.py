@@ -33,6 +33,18 @@ Entry points
         cf-1.com write-up, section 3.2)
   online_merge_normalized(s, v, bounds)           -- merge keeping O normalized
         after each block, with block-local max (notes, section 5)
+  attention_bwd_c(q, k, v, dO, scale, causal, heads=None)
+                                                  -- gradients dQ, dK, dV of
+        the square problem for an upstream gradient dO (C, OpenMP)
+  attention_bwd_np(q, k, v, dO, scale, causal)    -- the same gradients as
+        numpy matrix products
+
+Backward: the pages give the strategy (keep the row statistics, rebuild S
+and P from Q, K, V in the backward pass; notes, section 6) but no formulas.
+The gradients are the chain rule through O = P V, P = row-softmax(S),
+S = scale Q K^T over the visible pairs:
+    dV = P^T dO,  dP = dO V^T,  dS = P * (dP - rowsum(P * dP)),
+    dQ = scale dS K,  dK = scale dS^T Q.
 
 The two merge forms are here only to pin the claim that a block-by-block
 merge reproduces the whole-row softmax; the oracle itself never merges.
@@ -59,6 +71,12 @@ def _load():
             ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
             ctypes.c_int64, ctypes.c_double, ctypes.c_int, ctypes.c_void_p, ctypes.c_int64,
             ctypes.c_void_p, ctypes.c_void_p]
+        lib.oracle_attn_bwd_f64.restype = ctypes.c_int
+        lib.oracle_attn_bwd_f64.argtypes = [
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_double,
+            ctypes.c_int, ctypes.c_void_p, ctypes.c_int64,
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
         lib.oracle_max_threads.restype = ctypes.c_int
         lib.oracle_max_threads.argtypes = []
         _lib = lib
@@ -144,6 +162,55 @@ def attention_np(q, k, v, scale, causal, block_rows=1024):
                 O[b, h, r0:r1] = (p @ v[b, h]) / l
                 LSE[b, h, r0:r1] = m[:, 0] + np.log(l[:, 0])
     return O, LSE
+
+
+def attention_bwd_c(q, k, v, dO, scale, causal, heads=None):
+    """fp64 gradients of the square attention problem: q, k, v, dO are
+    float32 [B,H,N,d].  heads: optional flat (b*H + h) indices to compute.
+    Returns (dQ, dK, dV) float64, [B,H,N,d] each when heads is None, else
+    [len(heads), N, d]."""
+    q, k, v, dO = _as_f32(q), _as_f32(k), _as_f32(v), _as_f32(dO)
+    if not (q.shape == k.shape == v.shape == dO.shape):
+        raise ValueError("q, k, v, dO must share one [B,H,N,d] shape")
+    B, H, N, d = q.shape
+    if heads is None:
+        nh, harr = B * H, None
+    else:
+        harr = np.ascontiguousarray(heads, dtype=np.int64).ravel()
+        nh = harr.size
+    dQ = np.empty((nh, N, d))
+    dK = np.empty((nh, N, d))
+    dV = np.empty((nh, N, d))
+    rc = _load().oracle_attn_bwd_f64(
+        q.ctypes.data, k.ctypes.data, v.ctypes.data, dO.ctypes.data, B, H, N, d, float(scale),
+        int(bool(causal)), None if harr is None else harr.ctypes.data, nh,
+        dQ.ctypes.data, dK.ctypes.data, dV.ctypes.data)
+    if rc != 0:
+        raise RuntimeError("oracle_attn_bwd_f64 failed with code %d" % rc)
+    if heads is None:
+        return dQ.reshape(B, H, N, d), dK.reshape(B, H, N, d), dV.reshape(B, H, N, d)
+    return dQ, dK, dV
+
+
+def attention_bwd_np(q, k, v, dO, scale, causal):
+    """The same gradients as attention_bwd_c with whole-head numpy matrices
+    (small problems only: one N x N matrix per head)."""
+    q, k, v, dO = (np.asarray(x, dtype=np.float64) for x in (q, k, v, dO))
+    B, H, N, d = q.shape
+    dQ, dK, dV = np.empty_like(q), np.empty_like(q), np.empty_like(q)
+    for b in range(B):
+        for h in range(H):
+            s = float(scale) * (q[b, h] @ k[b, h].T)
+            if causal:
+                s = np.where(np.tril(np.ones((N, N), dtype=bool)), s, -np.inf)
+            p = np.exp(s - s.max(axis=1, keepdims=True))
+            p /= p.sum(axis=1, keepdims=True)
+            dp = dO[b, h] @ v[b, h].T
+            ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))
+            dV[b, h] = p.T @ dO[b, h]
+            dQ[b, h] = float(scale) * (ds @ k[b, h])
+            dK[b, h] = float(scale) * (ds.T @ q[b, h])
+    return dQ, dK, dV
 
 
 def _blocks(n, bounds):

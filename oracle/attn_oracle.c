@@ -119,3 +119,126 @@ int oracle_max_threads(void) {
   return 1;
 #endif
 }
+
+/* ------------------------------------------------------------------------
+ * Backward pass.  For an upstream gradient dO of O, the gradients of the
+ * attention above (square problem, Hkv == H, N queries and N keys) follow
+ * from the chain rule through O = P V, P = row-softmax(S), S = scale Q K^T:
+ *
+ *   dV_j  = sum_i P_ij dO_i
+ *   dP_ij = <dO_i, v_j>
+ *   dS_ij = P_ij (dP_ij - sum_j' P_ij' dP_ij')      (softmax Jacobian)
+ *   dQ_i  = scale * sum_j dS_ij k_j
+ *   dK_j  = scale * sum_i dS_ij q_i
+ *
+ * with i, j over the visible pairs only (j <= i when causal).  These are
+ * the quantities a recomputing backward pass rebuilds from Q, K, V and the
+ * saved row statistics (zzszmyf.github.io notes, section 6; aiqz.cc
+ * article, section 工程实现细节); the pages state that strategy, the formulas
+ * are the chain rule.  A row pass over i gives dQ and each row's (m, l, D); a
+ * key pass over j rebuilds P_ij from the same score expression and gives
+ * dK and dV.  No N x N buffer is formed.
+ * ---------------------------------------------------------------------- */
+
+static double dot_f32(const float* a, const float* b, int64_t d) {
+  double s = 0.0;
+  for (int64_t c = 0; c < d; ++c) s += (double)a[c] * (double)b[c];
+  return s;
+}
+
+/* Gradients for the heads listed in `heads` (flat b*H + h; NULL = every
+ * head, in order).  dQ, dK, dV are [nheads, N, d].  Returns 0 on success,
+ * 1 on a bad argument, 2 if scratch allocation fails. */
+int oracle_attn_bwd_f64(const float* q, const float* k, const float* v, const float* dO,
+                        int64_t B, int64_t H, int64_t N, int64_t d, double scale, int causal,
+                        const int64_t* heads, int64_t nheads,
+                        double* dQ, double* dK, double* dV) {
+  if (!q || !k || !v || !dO || !dQ || !dK || !dV || B < 1 || H < 1 || N < 1 || d < 1)
+    return 1;
+  if (heads == NULL) nheads = B * H;
+  if (nheads < 1) return 1;
+  for (int64_t t = 0; t < nheads; ++t)
+    if (heads && (heads[t] < 0 || heads[t] >= B * H)) return 1;
+  double* m = (double*)malloc(sizeof(double) * (size_t)N);
+  double* l = (double*)malloc(sizeof(double) * (size_t)N);
+  double* D = (double*)malloc(sizeof(double) * (size_t)N);
+  if (!m || !l || !D) {
+    free(m); free(l); free(D);
+    return 2;
+  }
+  int fail = 0;
+  for (int64_t t = 0; t < nheads; ++t) {
+    const int64_t bh = heads ? heads[t] : t;
+    const float* qh = q + bh * N * d;
+    const float* kh = k + bh * N * d;
+    const float* vh = v + bh * N * d;
+    const float* gh = dO + bh * N * d;
+    double* dq = dQ + t * N * d;
+    double* dk = dK + t * N * d;
+    double* dv = dV + t * N * d;
+
+    /* row pass: scores, softmax, dP, D_i = sum_j P_ij dP_ij, dS, dQ_i */
+#pragma omp parallel
+    {
+      double* s = (double*)malloc(sizeof(double) * (size_t)N);
+      double* gp = (double*)malloc(sizeof(double) * (size_t)N);
+      if (!s || !gp) {
+#pragma omp atomic write
+        fail = 1;
+      } else {
+#pragma omp for schedule(dynamic, 16)
+        for (int64_t i = 0; i < N; ++i) {
+          const int64_t nk = causal ? i + 1 : N;
+          double mx = -INFINITY;
+          for (int64_t j = 0; j < nk; ++j) {
+            s[j] = scale * dot_f32(qh + i * d, kh + j * d, d);
+            if (s[j] > mx) mx = s[j];
+          }
+          double sum = 0.0;
+          for (int64_t j = 0; j < nk; ++j) sum += exp(s[j] - mx);
+          double Di = 0.0;
+          for (int64_t j = 0; j < nk; ++j) {
+            gp[j] = dot_f32(gh + i * d, vh + j * d, d);      /* dP_ij */
+            Di += (exp(s[j] - mx) / sum) * gp[j];
+          }
+          m[i] = mx;
+          l[i] = sum;
+          D[i] = Di;
+          for (int64_t c = 0; c < d; ++c) dq[i * d + c] = 0.0;
+          for (int64_t j = 0; j < nk; ++j) {
+            const double p = exp(s[j] - mx) / sum;
+            const double ds = p * (gp[j] - Di);
+            for (int64_t c = 0; c < d; ++c) dq[i * d + c] += ds * (double)kh[j * d + c];
+          }
+          for (int64_t c = 0; c < d; ++c) dq[i * d + c] *= scale;
+        }
+      }
+      free(s);
+      free(gp);
+    }
+    if (fail) break;
+
+    /* key pass: P_ij rebuilt from the same scores, dV_j and dK_j */
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t j = 0; j < N; ++j) {
+      for (int64_t c = 0; c < d; ++c) {
+        dk[j * d + c] = 0.0;
+        dv[j * d + c] = 0.0;
+      }
+      for (int64_t i = causal ? j : 0; i < N; ++i) {
+        const double sij = scale * dot_f32(qh + i * d, kh + j * d, d);
+        const double p = exp(sij - m[i]) / l[i];
+        const double ds = p * (dot_f32(gh + i * d, vh + j * d, d) - D[i]);
+        for (int64_t c = 0; c < d; ++c) {
+          dv[j * d + c] += p * (double)gh[i * d + c];
+          dk[j * d + c] += ds * (double)qh[i * d + c];
+        }
+      }
+      for (int64_t c = 0; c < d; ++c) dk[j * d + c] *= scale;
+    }
+  }
+  free(m);
+  free(l);
+  free(D);
+  return fail ? 2 : 0;
+}
