@@ -28,6 +28,11 @@ fa_fwd_gqa; query head h reads K/V head h / (H/HKV)): with --decode the
 K/V bytes shrink by H/HKV; with a workload its K/V keep their first HKV
 heads (FLOPs unchanged).
 
+--bwd times the backward pass (fa_bwd) of the workload instead, with O and
+LSE from one fa_fwd call and dO drawn N(0,1) (seed 1000*cfg + 6); FLOPs are
+counted as 2.5x the forward's (five N^2 d products, causal halved; the
+kernels compute seven, recomputing S and dP for dQ).
+
 --copy-bytes S runs only a plain device-to-device copy of S bytes (used to
 calibrate the FETCH_SIZE / WRITE_SIZE counters) and exits.
 
@@ -283,6 +288,59 @@ def decode_bench(fa, args):
                       "peak_hbm_GBps": 8000}), flush=True)
 
 
+def bwd_bench(fa, args, w, x):
+    """Time fa_bwd on the workload; returns the JSON line."""
+    import torch
+    dev = torch.device("cuda:0")
+
+    from io_aware_softmax_fwd_amd import workloads as W
+
+    def up(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    rng = np.random.default_rng(1000 * w.cfg + 6)
+    g = rng.standard_normal((w.B, w.H, w.N, w.d), dtype=np.float32)
+    q, k, v = up(x["q_bits"]), up(x["k_bits"]), up(x["v_bits"])
+    dO = up(W.bf16_bits_rne(g))
+    o, lse = fa.fwd(q, k, v, scale=w.scale, causal=w.causal)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    ws = torch.empty(fa.fa_bwd_workspace_size(w.B, w.H, w.N, w.d), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    a = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dO.data_ptr(), lse.data_ptr(),
+         dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), w.B, w.H, w.N, w.d, w.scale, int(w.causal),
+         ws.data_ptr(), ws.numel(), stream.cuda_stream)
+    for _ in range(args.warmup):
+        st = fa.fa_bwd(*a)
+        if st != 0:
+            raise fa.FaError(st, "fa_bwd")
+    torch.cuda.synchronize()
+    for t in (dq, dk, dv):
+        if not torch.isfinite(t.float()).all():
+            raise RuntimeError("non-finite gradient")
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        fa.fa_bwd(*a)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = ev0.elapsed_time(ev1) / args.steps
+    flops = 2.5 * w.flops
+    return {"metric": "attention backward TFLOP/s (2.5x forward FLOPs: 5 N^2 d products, causal halved)",
+            "value": round(flops / (wall / args.steps) / 1e12, 2), "unit": "TFLOP/s", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall * 1e3 / args.steps, 4),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+            "data": "synthetic (seeded N(0,1) draws, bf16-rounded)",
+            "config": {"workload": w.name + "_bwd", "B": w.B, "H": w.H, "N": w.N, "d": w.d,
+                       "causal": w.causal, "flops": flops, "entry_point": "fa_bwd"},
+            "roofline": {"bound": "mfma", "achieved": round(flops / (ms * 1e-3) / 1e12, 2),
+                         "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                         "traffic": None, "kernel_ms": round(ms, 4),
+                         "executed_flops": 3.5 * w.flops}}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -295,6 +353,7 @@ def main():
     ap.add_argument("--splitkv", action="store_true")
     ap.add_argument("--decode", type=int, default=0, metavar="NK")
     ap.add_argument("--hkv", type=int, default=0, metavar="HKV")
+    ap.add_argument("--bwd", action="store_true")
     args = ap.parse_args()
 
     if args.summarize:
@@ -325,6 +384,11 @@ def main():
     w = W.WORKLOADS[args.workload]
     x = W.make_inputs(w)
     dev = torch.device("cuda:0")
+    if args.bwd:
+        if w.dtype != "bf16":
+            raise SystemExit("--bwd needs a bf16 workload")
+        print(json.dumps(bwd_bench(fa, args, w, x)), flush=True)
+        return
     hkv = args.hkv or w.H
     if args.hkv:
         if w.dtype != "bf16" or w.H % hkv != 0:

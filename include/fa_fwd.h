@@ -154,6 +154,36 @@ int fa_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse,
  * (1 if an argument is out of range).  Host only, no HIP call. */
 int fa_fwd_gqa_num_splits(int B, int H, int Hkv, int Nq, int Nk, int causal, int num_cus);
 
+/*
+ * Attention backward (bf16), by recomputation: the gradients of
+ * O = softmax(scale * Q K^T) V for an upstream gradient dO, rebuilt from Q,
+ * K, V and the forward pass's O and LSE without any N x N buffer
+ * (zzszmyf.github.io notes "FlashAttention 原理是什么", section 6; aiqz.cc
+ * Flash Attention IO article, section 工程实现细节).  With P_ij =
+ * exp(scale <q_i, k_j> - LSE_i) over the visible pairs,
+ *     dV = P^T dO,  dS = P * (dO V^T - D),  D_i = <dO_i, O_i>,
+ *     dQ = scale dS K,  dK = scale dS^T Q.
+ *   q, k, v, o, dout : device pointers, [B,H,N,d] bf16 (o and lse as written
+ *                      by fa_fwd for the same q, k, v, scale and causal).
+ *   lse              : [B,H,N] fp32.
+ *   dq, dk, dv       : [B,H,N,d] bf16, written (round to nearest even).
+ *   workspace        : device buffer of at least fa_bwd_workspace_size(...)
+ *                      bytes, 16-byte aligned; scratch for the per-row D.
+ *   B, H, N, d, scale, causal : as for fa_fwd.
+ * dq, dk, dv and the workspace must not overlap each other or any input.
+ * Two kernels are queued on `stream` (dQ with D, then dK and dV); neither
+ * uses atomics, so results are reproducible bit for bit.  Errors as for
+ * fa_fwd, plus FA_ERR_WORKSPACE.
+ */
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+           const float* lse, void* dq, void* dk, void* dv, int B, int H, int N, int d,
+           float scale, int causal, void* workspace, size_t workspace_bytes,
+           hipStream_t stream);
+
+/* Bytes of workspace fa_bwd needs (0 if an argument is out of range).
+ * Host only, no HIP call. */
+size_t fa_bwd_workspace_size(int B, int H, int N, int d);
+
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* fa_strerror(int status);
 

@@ -14,6 +14,9 @@ Low level (same names and arguments as the C functions, raw pointers):
     fa_fwd_gqa(q, k, v, o, lse, B, H, Hkv, Nq, Nk, d, scale, causal,
                num_splits, workspace, workspace_bytes, stream) -> status
     fa_fwd_gqa_num_splits(B, H, Hkv, Nq, Nk, causal, num_cus)  -> count
+    fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, scale, causal,
+           workspace, workspace_bytes, stream)                 -> status
+    fa_bwd_workspace_size(B, H, N, d)                          -> bytes
     fa_strerror(status)                                        -> str
 High level (torch tensors on a ROCm device):
     fwd(q, k, v, scale=None, causal=False, out=None, lse=None) -> (o, lse)
@@ -21,6 +24,8 @@ High level (torch tensors on a ROCm device):
                 workspace=None)                                -> (o, lse)
     fwd_gqa(q, k, v, scale=None, causal=False, num_splits=1,
             workspace=None)                                    -> (o, lse)
+    bwd(q, k, v, o, lse, dout, scale=None, causal=False,
+        workspace=None)                                        -> (dq, dk, dv)
 """
 import ctypes
 import math
@@ -42,7 +47,8 @@ FA_ERR_SPLITS = 10
 FA_ERR_HEADS = 11
 
 EXPORTED = ("fa_fwd", "fa_fwd_f32", "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_size",
-            "fa_fwd_splitkv_num_splits", "fa_fwd_gqa", "fa_fwd_gqa_num_splits", "fa_strerror")
+            "fa_fwd_splitkv_num_splits", "fa_fwd_gqa", "fa_fwd_gqa_num_splits", "fa_bwd",
+            "fa_bwd_workspace_size", "fa_strerror")
 
 _lib = None
 
@@ -82,6 +88,12 @@ def load():
                                 ctypes.c_size_t, ctypes.c_void_p])
     lib.fa_fwd_gqa_num_splits.restype = ctypes.c_int
     lib.fa_fwd_gqa_num_splits.argtypes = [ctypes.c_int] * 7
+    lib.fa_bwd.restype = ctypes.c_int
+    lib.fa_bwd.argtypes = ([ctypes.c_void_p] * 9 + [ctypes.c_int] * 4 +
+                           [ctypes.c_float, ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t,
+                            ctypes.c_void_p])
+    lib.fa_bwd_workspace_size.restype = ctypes.c_size_t
+    lib.fa_bwd_workspace_size.argtypes = [ctypes.c_int] * 4
     lib.fa_strerror.restype = ctypes.c_char_p
     lib.fa_strerror.argtypes = [ctypes.c_int]
     _lib = lib
@@ -118,6 +130,16 @@ def fa_fwd_gqa(q, k, v, o, lse, B, H, Hkv, Nq, Nk, d, scale, causal, num_splits,
 
 def fa_fwd_gqa_num_splits(B, H, Hkv, Nq, Nk, causal, num_cus):
     return int(load().fa_fwd_gqa_num_splits(B, H, Hkv, Nq, Nk, causal, num_cus))
+
+
+def fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, scale, causal, workspace,
+           workspace_bytes, stream):
+    return load().fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, scale, causal, workspace,
+                         workspace_bytes, stream)
+
+
+def fa_bwd_workspace_size(B, H, N, d):
+    return int(load().fa_bwd_workspace_size(B, H, N, d))
 
 
 def fa_strerror(status):
@@ -248,3 +270,38 @@ def fwd_gqa(q, k, v, scale=None, causal=False, num_splits=1, workspace=None,
     if st != FA_OK:
         raise FaError(st, "fa_fwd_gqa")
     return out, lse
+
+
+def bwd(q, k, v, o, lse, dout, scale=None, causal=False, workspace=None, stream=None):
+    """Attention backward of bf16 torch tensors q, k, v, o, dout [B,H,N,d] and
+    the forward's lse [B,H,N] (fp32), all contiguous on the GPU.  Returns
+    (dq, dk, dv) as bf16 tensors; the workspace (uint8 device tensor) is
+    allocated here if not given."""
+    import torch
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
+        if not isinstance(t, torch.Tensor):
+            raise TypeError("%s must be a torch.Tensor" % name)
+        if t.device.type != "cuda" or not t.is_contiguous() or t.dim() != 4:
+            raise ValueError("%s must be a contiguous 4-D GPU tensor" % name)
+        if t.dtype != torch.bfloat16:
+            raise TypeError("%s must be bfloat16" % name)
+        if t.shape != q.shape:
+            raise ValueError("%s must have q's shape" % name)
+    B, H, N, d = q.shape
+    if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 [B, H, N] tensor")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if workspace is None:
+        workspace = torch.empty(max(1, fa_bwd_workspace_size(B, H, N, d)), dtype=torch.uint8,
+                                device=q.device)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    st = fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
+                lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, d,
+                float(scale), int(bool(causal)), workspace.data_ptr(),
+                workspace.numel() * workspace.element_size(), stream)
+    if st != FA_OK:
+        raise FaError(st, "fa_bwd")
+    return dq, dk, dv

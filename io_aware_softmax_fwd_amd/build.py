@@ -1,5 +1,7 @@
 """Build libfa_fwd.so (HIP kernels for gfx950 + the C entry points) in-tree.
 
+The objects of the four sources are compiled in parallel.
+
     python -m io_aware_softmax_fwd_amd.build
 
 Packed-fp32 VALU forms are disabled for the device code; every source is
@@ -14,7 +16,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libfa_fwd.so")
-SOURCES = ["fa_api.cpp", "fa_fwd_bf16.hip", "fa_fwd_f32.hip"]
+SOURCES = ["fa_api.cpp", "fa_fwd_bf16.hip", "fa_fwd_f32.hip", "fa_bwd_bf16.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 DEVICE_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
@@ -26,20 +28,26 @@ def build(verbose: bool = False) -> str:
     objs = []
     bdir = os.path.join(PKG, "_build")
     os.makedirs(bdir, exist_ok=True)
+    procs = []
     for src in SOURCES:
         obj = os.path.join(bdir, src + ".o")
         cmd = [HIPCC, *DEVICE_FLAGS, "-I", INCLUDE, "-I", CSRC, "-c",
                os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
-        r = subprocess.run(cmd, capture_output=True, text=True)
-        errs = "\n".join(l for l in (r.stderr or "").splitlines()
-                         if "packed-fp32-ops" not in l)
-        if r.returncode != 0:
-            raise RuntimeError("hipcc failed for %s:\n%s" % (src, errs))
-        if errs.strip() and verbose:
-            print(errs)
+        procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE,
+                                            text=True)))
         objs.append(obj)
+    failed = []
+    for src, pr in procs:
+        _, err = pr.communicate()
+        errs = "\n".join(l for l in (err or "").splitlines() if "packed-fp32-ops" not in l)
+        if pr.returncode != 0:
+            failed.append("hipcc failed for %s:\n%s" % (src, errs))
+        elif errs.strip() and verbose:
+            print(errs)
+    if failed:
+        raise RuntimeError("\n".join(failed))
     tmp = LIB + ".tmp%d" % os.getpid()
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -100,6 +100,32 @@ int choose_splits(int B, int H, int Hkv, int Nq, int Nk, int causal, int num_cus
   return (int)std::max<int64_t>(1, std::min<int64_t>(std::min<int64_t>(want, most), kMaxSplits));
 }
 
+int validate_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                 const float* lse, const void* dq, const void* dk, const void* dv, int B, int H, int N,
+                 int d, float scale, int causal, const void* ws, size_t ws_bytes) {
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return FA_ERR_NULL;
+  if (B < 1 || H < 1 || N < 1) return FA_ERR_SHAPE;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED_D;
+  const int64_t rows = (int64_t)B * H * N;
+  if (rows * d >= kMaxElems) return FA_ERR_SHAPE;
+  if ((int64_t)N * d * 2 >= (int64_t(1) << 31)) return FA_ERR_SHAPE;
+  if (!(scale > 0.f) || !isfinite(scale)) return FA_ERR_SCALE;
+  if (causal != 0 && causal != 1) return FA_ERR_CAUSAL;
+  const void* all[] = {q, k, v, o, dout, lse, dq, dk, dv, ws};
+  for (const void* p : all)
+    if (p && misaligned(p)) return FA_ERR_ALIGN;
+  const int64_t wb = fa::bwd_workspace_bytes(B, H, N);
+  if (!ws || (int64_t)ws_bytes < wb) return FA_ERR_WORKSPACE;
+  // outputs (dq, dk, dv, workspace) overlap nothing else
+  const int64_t tb = rows * d * 2, lb = rows * 4;
+  const void* ptr[] = {q, k, v, o, dout, lse, dq, dk, dv, ws};
+  const int64_t len[] = {tb, tb, tb, tb, tb, lb, tb, tb, tb, wb};
+  for (int a = 6; a < 10; ++a)
+    for (int b = 0; b < 10; ++b)
+      if (a != b && overlap(ptr[a], len[a], ptr[b], len[b])) return FA_ERR_ALIAS;
+  return FA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -159,6 +185,21 @@ int fa_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse,
   const fa::GqaProblem p{q, k, v, o, lse, B, H, Hkv, Nq, Nk, d, scale, causal, num_splits,
                          num_splits > 1 ? workspace : nullptr};
   return fa::launch_fwd_bf16(p, stream) == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+size_t fa_bwd_workspace_size(int B, int H, int N, int d) {
+  if (B < 1 || H < 1 || N < 1 || (d != 64 && d != 128)) return 0;
+  return (size_t)fa::bwd_workspace_bytes(B, H, N);
+}
+
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+           const float* lse, void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale,
+           int causal, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  const int st = validate_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, scale, causal,
+                              workspace, workspace_bytes);
+  if (st != FA_OK) return st;
+  const fa::BwdProblem p{q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, scale, causal, workspace};
+  return fa::launch_bwd_bf16(p, stream) == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
 const char* fa_strerror(int status) {

@@ -1,0 +1,541 @@
+// bf16 attention backward on the gfx950 matrix cores, by recomputation.
+//
+// The forward pass keeps only O and one log-sum-exp per row; the backward
+// pass re-reads Q, K, V in tiles and rebuilds the scores and probabilities
+// on chip instead of storing the N x N matrices (zzszmyf.github.io notes
+// "FlashAttention 原理是什么", section 6; aiqz.cc Flash Attention IO article,
+// section 工程实现细节).  With P = exp(scale*QK^T - LSE) (row statistics
+// from the forward pass) the gradients are the chain rule
+//     dV = P^T dO,   dP = dO V^T,   dS = P * (dP - D),   D_i = <dO_i, O_i>,
+//     dQ = scale * dS K,   dK = scale * dS^T Q
+// (D_i equals sum_j P_ij dP_ij because O_i = sum_j P_ij v_j).
+//
+// Two kernels, no atomics, so every result is reproducible bit for bit:
+//   bwd_dq_kernel    one workgroup per 128 query rows.  Q and dO stay in
+//                    registers, K and V tiles stream through LDS; it also
+//                    writes D for the second kernel.  Products are taken
+//                    transposed as in the forward kernel (S^T = K Q^T,
+//                    dP^T = V dO^T, dQ^T += K^T dS^T) so each lane owns one
+//                    query and its row statistics are lane constants.
+//   bwd_dkdv_kernel  one workgroup per 128 keys.  K and V stay in registers,
+//                    Q and dO tiles (with the rows' LSE and D) stream through
+//                    LDS; S = Q K^T and dP = dO V^T put one key per lane, and
+//                    dV^T += dO^T P, dK^T += Q^T dS take the probabilities
+//                    straight from the accumulators as B operands, with the
+//                    transposed operand read by ds_read_b64_tr_b16.
+// Both recompute S and dP: seven N^2 d products in all against five for a
+// single kernel that adds dQ with atomics, traded for determinism.
+#include <math.h>
+
+#include "fa_device.h"
+#include "fa_internal.h"
+
+namespace fa {
+namespace {
+
+constexpr int kBwdWaves = 4;
+constexpr int kBwdThreads = 64 * kBwdWaves;
+constexpr int kRows = 64;        // rows per streamed tile (keys, or queries)
+
+// LDS row strides in bytes.  An operand read only row-major (16-byte
+// fragment reads, 16 consecutive rows per access group) uses 2D + 16
+// bytes: stride/4 is 4 (mod 64) banks times an odd number, so the 16 rows
+// start on distinct bank quads.  An operand read both row-major and
+// transposed (ds_read_b64_tr_b16: 4 rows x 32 bytes per 32 lanes) uses
+// stride/4 = 12 (d=128) or 52 (d=64) mod 64: still conflict-free row
+// reads, and at most 2-way conflicts on the transposed reads.
+template <int D> struct BwdCfg {
+  static constexpr int rowStride = 2 * D + 16;
+  static constexpr int bothStride = D == 128 ? 304 : 208;
+};
+
+// LDS-DMA of one 64-row tile of a [N, D] bf16 head into an LDS buffer of
+// STRIDE-byte rows, spread over the four waves in 1 KB blocks.
+template <int D, int STRIDE> struct Dma {
+  static constexpr int bytes = kRows * STRIDE;
+  static constexpr int nblk = bytes / 1024;
+  static constexpr int perWave = (nblk + kBwdWaves - 1) / kBwdWaves;
+  static_assert(bytes % 1024 == 0, "tile must be whole 1 KB blocks");
+  int off[perWave];
+  __device__ void setup(int wave, int lane) {
+#pragma unroll
+    for (int i = 0; i < perWave; ++i) off[i] = dma_offset<D>((wave + kBwdWaves * i) * 64 + lane, STRIDE);
+  }
+  __device__ void issue(const unsigned short* head, int r0, int N, unsigned char* dst, int wave) const {
+#if defined(__HIP_DEVICE_COMPILE__)
+    const __amdgpu_buffer_rsrc_t r = tile_rsrc<D>(head, r0, N);
+#pragma unroll
+    for (int i = 0; i < perWave; ++i) {
+      const int blk = wave + kBwdWaves * i;
+      if (nblk % kBwdWaves == 0 || blk < nblk)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(dst + blk * 1024), 16, off[i], 0, 0, 0);
+    }
+#endif
+  }
+};
+
+// Transposed 32-row x 16-key operand from a row-major LDS tile: `src` is this
+// lane's address of key row 0 of the 16-key group; the two reads (rows +0 and
+// +8) give the 8 keys that the accumulator layout assigns to the lane.
+template <int STRIDE>
+__device__ __forceinline__ bf16x8 tr_operand(const unsigned char* src) {
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)src);
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(src + 8 * STRIDE));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// Lane offset of the transposed reads: in each 16-lane group g, lane 4e + j
+// addresses row 4*(g/2) + e and columns 16*(g%2) + 4j .. +3 of a 32-column
+// block.
+template <int STRIDE>
+__device__ __forceinline__ int tr_offset(int lane) {
+  const int g = lane >> 4, e = (lane >> 2) & 3, j = lane & 3;
+  return (4 * (g >> 1) + e) * STRIDE + 2 * (16 * (g & 1) + 4 * j);
+}
+
+// Load this lane's share of one row as MFMA B-operand fragments: dims
+// 16*ks + 8*hl .. +7 for ks < D/16 (zero when the row is out of range).
+template <int D>
+__device__ __forceinline__ void load_row_fragments(const unsigned short* row, bool valid, int hl,
+                                                   bf16x8 (&f)[D / 16]) {
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) {
+    u32x4 raw = {0u, 0u, 0u, 0u};
+    if (valid) raw = *reinterpret_cast<const u32x4*>(row + 16 * ks + 8 * hl);
+    f[ks] = __builtin_bit_cast(bf16x8, raw);
+  }
+}
+
+// Store a transposed fp32 accumulator (rows = head dims, lane = one output
+// row) times `mul` as bf16: dims 32*db + 8*g + 4*hl .. +3 from elements
+// 4g .. 4g+3 of block db.
+template <int D>
+__device__ __forceinline__ void store_rowT(unsigned short* row, const f32x16 (&acc)[D / 32], float mul,
+                                           int hl) {
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int dim = 32 * db + 8 * g + 4 * hl;
+      const u32x2 w = {pack_bf16x2(acc[db][4 * g] * mul, acc[db][4 * g + 1] * mul),
+                       pack_bf16x2(acc[db][4 * g + 2] * mul, acc[db][4 * g + 3] * mul)};
+      *reinterpret_cast<u32x2*>(row + dim) = w;
+    }
+}
+
+// ----------------------------------------------------------------- dQ kernel
+template <int D, bool CAUSAL>
+struct BwdQ {
+  static constexpr int KS = D / 16, DB = D / 32;
+  static constexpr int KSTR = BwdCfg<D>::bothStride, VSTR = BwdCfg<D>::rowStride;
+
+  const unsigned short* kh;
+  const unsigned short* vh;
+  int N, wave, l32, hl, qi;
+  float c, lse2, Drow;
+  bf16x8 qf[KS];          // Q row of this lane's query (B operand of S^T = K Q^T)
+  bf16x8 gf[KS];          // dO row (B operand of dP^T = V dO^T)
+  f32x16 acc[DB];         // dQ^T: lane holds query l%32
+  Dma<D, KSTR> kd;
+  Dma<D, VSTR> vd;
+  int k_rd, v_rd, kt_rd;
+  unsigned char* kbuf[2];
+  unsigned char* vbuf[2];
+
+  template <int B>
+  __device__ void issue(int k0) {
+    kd.issue(kh, k0, N, kbuf[B], wave);
+    vd.issue(vh, k0, N, vbuf[B], wave);
+  }
+
+  template <bool MASK, int PAR>
+  __device__ void consume(int k0) {
+    const unsigned char* kt = kbuf[PAR];
+    const unsigned char* vt = vbuf[PAR];
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+      f32x16 s, dp;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        s[r] = 0.f;
+        dp[r] = 0.f;
+      }
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kt + k_rd + 32 * h2 * KSTR + 32 * ks);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], s, 0, 0, 0);
+        const bf16x8 vf = *reinterpret_cast<const bf16x8*>(vt + v_rd + 32 * h2 * VSTR + 32 * ks);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, gf[ks], dp, 0, 0, 0);
+      }
+      // dS^T = P^T (dP^T - D); key = k0 + 32*h2 + (r&3) + 8*(r>>2) + 4*hl
+      const int lim = (CAUSAL ? min(qi, N - 1) : N - 1) - k0 - 32 * h2 - 4 * hl;
+      bf16x8 dsf[2];
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        u32x4 w;
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          const int r = 8 * half + e;
+          float p0 = __builtin_amdgcn_exp2f(fmaf(s[r], c, -lse2));
+          float p1 = __builtin_amdgcn_exp2f(fmaf(s[r + 1], c, -lse2));
+          if (MASK) {
+            if ((r & 3) + 8 * (r >> 2) > lim) p0 = 0.f;
+            if (((r + 1) & 3) + 8 * ((r + 1) >> 2) > lim) p1 = 0.f;
+          }
+          w[e / 2] = pack_bf16x2(p0 * (dp[r] - Drow), p1 * (dp[r + 1] - Drow));
+        }
+        dsf[half] = __builtin_bit_cast(bf16x8, w);
+      }
+      // dQ^T += K^T dS^T over the 32 keys, two 16-key steps
+#pragma unroll
+      for (int ps = 0; ps < 2; ++ps)
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const bf16x8 kT = tr_operand<KSTR>(kt + kt_rd + (32 * h2 + 16 * ps) * KSTR + 64 * db);
+          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kT, dsf[ps], acc[db], 0, 0, 0);
+        }
+    }
+  }
+
+  template <bool MASK, int PAR>
+  __device__ void step(int j, int t_end, int wlast) {
+    const int k0 = j * kRows;
+    if (j + 1 < t_end) issue<PAR ^ 1>(k0 + kRows);
+    if (!MASK || !CAUSAL || k0 <= wlast) consume<MASK, PAR>(k0);
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+  }
+};
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(
+    const unsigned short* __restrict__ q, const unsigned short* __restrict__ k,
+    const unsigned short* __restrict__ v, const unsigned short* __restrict__ o,
+    const unsigned short* __restrict__ dout, const float* __restrict__ lse,
+    unsigned short* __restrict__ dq, float* __restrict__ dws, int N, int BH, int n_qtiles,
+    float scale) {
+  using F = BwdQ<D, CAUSAL>;
+  __shared__ __attribute__((aligned(1024))) unsigned char k_lds0[Dma<D, F::KSTR>::bytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char k_lds1[Dma<D, F::KSTR>::bytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char v_lds0[Dma<D, F::VSTR>::bytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char v_lds1[Dma<D, F::VSTR>::bytes];
+  constexpr int KS = D / 16, DB = D / 32, BR = 32 * kBwdWaves;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int bh = blockIdx.x % BH;
+  const int qt = n_qtiles - 1 - blockIdx.x / BH;   // heaviest causal tiles first
+  const int q0 = qt * BR;
+  const int64_t head = (int64_t)bh * N * D;
+
+  F f;
+  f.kbuf[0] = k_lds0;
+  f.kbuf[1] = k_lds1;
+  f.vbuf[0] = v_lds0;
+  f.vbuf[1] = v_lds1;
+  f.kh = k + head;
+  f.vh = v + head;
+  f.N = N;
+  f.wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  f.l32 = lane & 31;
+  f.hl = lane >> 5;
+  const int qw = q0 + 32 * f.wave;
+  f.qi = qw + f.l32;
+  f.c = scale * kLog2e;
+  const bool valid = f.qi < N;
+  const unsigned short* qrow = q + head + (int64_t)f.qi * D;
+  load_row_fragments<D>(qrow, valid, f.hl, f.qf);
+  load_row_fragments<D>(dout + head + (int64_t)f.qi * D, valid, f.hl, f.gf);
+  {
+    // D_i = <dO_i, O_i>: this lane's 64 dims, then the other half-wave's
+    bf16x8 of[KS];
+    load_row_fragments<D>(o + head + (int64_t)f.qi * D, valid, f.hl, of);
+    float part = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        const bf16x2 a = {f.gf[ks][e], f.gf[ks][e + 1]};
+        const bf16x2 b = {of[ks][e], of[ks][e + 1]};
+        part = __builtin_amdgcn_fdot2_f32_bf16(a, b, part, false);
+      }
+    f.Drow = sum_across_halves(part);
+  }
+  f.lse2 = valid ? lse[(int64_t)bh * N + f.qi] * kLog2e : 0.f;
+  if (valid && f.hl == 0) dws[(int64_t)bh * N + f.qi] = f.Drow;
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) f.acc[db][r] = 0.f;
+  f.kd.setup(f.wave, lane);
+  f.vd.setup(f.wave, lane);
+  f.k_rd = f.l32 * F::KSTR + 16 * f.hl;
+  f.v_rd = f.l32 * F::VSTR + 16 * f.hl;
+  f.kt_rd = tr_offset<F::KSTR>(lane);
+
+  const int kv_end = CAUSAL ? min(N, q0 + BR) : N;
+  const int n_tiles = (kv_end + kRows - 1) / kRows;
+  const int n_full = CAUSAL ? min(q0 + 1, N) / kRows : N / kRows;
+  const int wlast = qw + 31;   // last query of the wave (causal skip)
+
+  f.template issue<0>(0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  int j = 0;
+  const int full_end = min(n_tiles, n_full);
+  for (; j + 1 < full_end; j += 2) {
+    f.template step<false, 0>(j, n_tiles, wlast);
+    f.template step<false, 1>(j + 1, n_tiles, wlast);
+  }
+  if (j < full_end) {
+    f.template step<false, 0>(j, n_tiles, wlast);
+    ++j;
+  }
+  for (; j < n_tiles; ++j) {
+    if (j & 1) f.template step<true, 1>(j, n_tiles, wlast);
+    else       f.template step<true, 0>(j, n_tiles, wlast);
+  }
+  if (valid) store_rowT<D>(dq + head + (int64_t)f.qi * D, f.acc, scale, f.hl);
+}
+
+// ------------------------------------------------------------- dK/dV kernel
+template <int D, bool CAUSAL>
+struct BwdKV {
+  static constexpr int KS = D / 16, DB = D / 32;
+  static constexpr int STR = BwdCfg<D>::bothStride;
+
+  const unsigned short* qh;
+  const unsigned short* gh;
+  const float* lseh;
+  const float* dh;
+  int N, wave, lane, l32, hl, kj;
+  float c;
+  bf16x8 kf[KS];          // K row of this lane's key (B operand of S = Q K^T)
+  bf16x8 vf[KS];          // V row (B operand of dP = dO V^T)
+  f32x16 dk[DB];          // dK^T: lane holds key l%32
+  f32x16 dv[DB];          // dV^T
+  Dma<D, STR> qd;
+  Dma<D, STR> gd;
+  int q_rd, t_rd;
+  float stat;             // waves 0 and 1: the LSE*log2(e) or D of row `lane` of the next tile
+  unsigned char* qbuf[2];
+  unsigned char* gbuf[2];
+  float* lbuf[2];
+  float* dbuf[2];
+
+  // Queue tile q0 (Q, dO by LDS-DMA; LSE and D into registers of waves 0, 1).
+  template <int B>
+  __device__ void issue(int q0) {
+    qd.issue(qh, q0, N, qbuf[B], wave);
+    gd.issue(gh, q0, N, gbuf[B], wave);
+    const int r = q0 + lane;
+    if (wave == 0) stat = r < N ? lseh[r] * kLog2e : INFINITY;   // rows >= N get P = 0
+    else if (wave == 1) stat = r < N ? dh[r] : 0.f;
+  }
+  // After the tile's loads have landed: make its row statistics visible.
+  template <int B>
+  __device__ void publish() {
+    if (wave == 0) lbuf[B][lane] = stat;
+    else if (wave == 1) dbuf[B][lane] = stat;
+  }
+
+  template <bool MASK, int PAR>
+  __device__ void consume(int q0) {
+    const unsigned char* qt = qbuf[PAR];
+    const unsigned char* gt = gbuf[PAR];
+    const float* lt = lbuf[PAR];
+    const float* dt = dbuf[PAR];
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+      // causal: every query of this half precedes every key of the wave
+      if (MASK && CAUSAL && q0 + 32 * h2 + 31 < kj - l32) continue;
+      f32x16 s, dp;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        s[r] = 0.f;
+        dp[r] = 0.f;
+      }
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const bf16x8 qa = *reinterpret_cast<const bf16x8*>(qt + q_rd + 32 * h2 * STR + 32 * ks);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[ks], s, 0, 0, 0);
+        const bf16x8 ga = *reinterpret_cast<const bf16x8*>(gt + q_rd + 32 * h2 * STR + 32 * ks);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga, vf[ks], dp, 0, 0, 0);
+      }
+      // row statistics of the lane's 16 queries: 32*h2 + 8t + 4*hl + (0..3)
+      float4 L[4], Dd[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        L[t] = *reinterpret_cast<const float4*>(lt + 32 * h2 + 8 * t + 4 * hl);
+        Dd[t] = *reinterpret_cast<const float4*>(dt + 32 * h2 + 8 * t + 4 * hl);
+      }
+      // query of element r: q0 + 32*h2 + (r&3) + 8*(r>>2) + 4*hl; key kj
+      const int qmin = kj - (q0 + 32 * h2 + 4 * hl);   // masked when (r&3) + 8*(r>>2) < qmin
+      bf16x8 pf[2], dsf[2];
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        u32x4 wp, wd;
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          const int r = 8 * half + e;
+          const float* Lr = reinterpret_cast<const float*>(&L[r >> 2]);
+          const float* Dr = reinterpret_cast<const float*>(&Dd[r >> 2]);
+          float p0 = __builtin_amdgcn_exp2f(fmaf(s[r], c, -Lr[r & 3]));
+          float p1 = __builtin_amdgcn_exp2f(fmaf(s[r + 1], c, -Lr[(r + 1) & 3]));
+          if (MASK && CAUSAL) {
+            if ((r & 3) + 8 * (r >> 2) < qmin) p0 = 0.f;
+            if (((r + 1) & 3) + 8 * ((r + 1) >> 2) < qmin) p1 = 0.f;
+          }
+          wp[e / 2] = pack_bf16x2(p0, p1);
+          wd[e / 2] = pack_bf16x2(p0 * (dp[r] - Dr[r & 3]), p1 * (dp[r + 1] - Dr[(r + 1) & 3]));
+        }
+        pf[half] = __builtin_bit_cast(bf16x8, wp);
+        dsf[half] = __builtin_bit_cast(bf16x8, wd);
+      }
+      // dV^T += dO^T P and dK^T += Q^T dS over the 32 queries
+#pragma unroll
+      for (int ps = 0; ps < 2; ++ps)
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const int src = t_rd + (32 * h2 + 16 * ps) * STR + 64 * db;
+          const bf16x8 gT = tr_operand<STR>(gt + src);
+          dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(gT, pf[ps], dv[db], 0, 0, 0);
+          const bf16x8 qT = tr_operand<STR>(qt + src);
+          dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qT, dsf[ps], dk[db], 0, 0, 0);
+        }
+    }
+  }
+
+  // Consume tile j from buffers PAR while tile `next` (if any) lands in the
+  // other buffers.
+  template <bool MASK, int PAR>
+  __device__ void step(int j, int next, bool has_next) {
+    if (has_next) issue<PAR ^ 1>(next * kRows);
+    consume<MASK, PAR>(j * kRows);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    if (has_next) publish<PAR ^ 1>();
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+  }
+};
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
+    const unsigned short* __restrict__ q, const unsigned short* __restrict__ k,
+    const unsigned short* __restrict__ v, const unsigned short* __restrict__ dout,
+    const float* __restrict__ lse, const float* __restrict__ dws, unsigned short* __restrict__ dk,
+    unsigned short* __restrict__ dv, int N, int BH, float scale) {
+  using F = BwdKV<D, CAUSAL>;
+  __shared__ __attribute__((aligned(1024))) unsigned char q_lds0[Dma<D, F::STR>::bytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char q_lds1[Dma<D, F::STR>::bytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char g_lds0[Dma<D, F::STR>::bytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char g_lds1[Dma<D, F::STR>::bytes];
+  __shared__ __attribute__((aligned(16))) float l_lds0[kRows];
+  __shared__ __attribute__((aligned(16))) float l_lds1[kRows];
+  __shared__ __attribute__((aligned(16))) float d_lds0[kRows];
+  __shared__ __attribute__((aligned(16))) float d_lds1[kRows];
+  constexpr int DB = D / 32, BK = 32 * kBwdWaves;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int bh = blockIdx.x % BH;
+  const int kt = blockIdx.x / BH;     // smallest keys first: they meet the most causal queries
+  const int k0 = kt * BK;
+  const int64_t head = (int64_t)bh * N * D;
+
+  F f;
+  f.qbuf[0] = q_lds0;
+  f.qbuf[1] = q_lds1;
+  f.gbuf[0] = g_lds0;
+  f.gbuf[1] = g_lds1;
+  f.lbuf[0] = l_lds0;
+  f.lbuf[1] = l_lds1;
+  f.dbuf[0] = d_lds0;
+  f.dbuf[1] = d_lds1;
+  f.qh = q + head;
+  f.gh = dout + head;
+  f.lseh = lse + (int64_t)bh * N;
+  f.dh = dws + (int64_t)bh * N;
+  f.N = N;
+  f.wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  f.lane = lane;
+  f.l32 = lane & 31;
+  f.hl = lane >> 5;
+  f.kj = k0 + 32 * f.wave + f.l32;
+  f.c = scale * kLog2e;
+  const bool valid = f.kj < N;
+  load_row_fragments<D>(k + head + (int64_t)f.kj * D, valid, f.hl, f.kf);
+  load_row_fragments<D>(v + head + (int64_t)f.kj * D, valid, f.hl, f.vf);
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      f.dk[db][r] = 0.f;
+      f.dv[db][r] = 0.f;
+    }
+  f.qd.setup(f.wave, lane);
+  f.gd.setup(f.wave, lane);
+  f.q_rd = f.l32 * F::STR + 16 * f.hl;
+  f.t_rd = tr_offset<F::STR>(lane);
+
+  // Query tiles that see any of this workgroup's keys: [t0, t1).  Causal:
+  // tiles before t_full hold a query that precedes one of the keys and are
+  // masked; they are consumed last (the loop walks down from t1 - 1).
+  const int t0 = CAUSAL ? k0 / kRows : 0;
+  const int t1 = (N + kRows - 1) / kRows;
+  const int t_full = CAUSAL ? min(t1, (k0 + BK - 1 + kRows - 1) / kRows) : t0;
+
+  if (t0 < t1) {
+    f.template issue<0>((t1 - 1) * kRows);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    f.template publish<0>();
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __syncthreads();
+    int j = t1 - 1;
+    for (; j - 1 >= t_full; j -= 2) {
+      f.template step<false, 0>(j, j - 1, true);
+      f.template step<false, 1>(j - 1, j - 2, j - 2 >= t0);
+    }
+    if (j >= t_full) {
+      f.template step<false, 0>(j, j - 1, j - 1 >= t0);
+      --j;
+    }
+    for (; j >= t0; --j) {
+      if ((t1 - 1 - j) & 1) f.template step<true, 1>(j, j - 1, j - 1 >= t0);
+      else                  f.template step<true, 0>(j, j - 1, j - 1 >= t0);
+    }
+  }
+  if (valid) {
+    store_rowT<D>(dk + head + (int64_t)f.kj * D, f.dk, scale, f.hl);
+    store_rowT<D>(dv + head + (int64_t)f.kj * D, f.dv, 1.f, f.hl);
+  }
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch_bwd(const BwdProblem& p, hipStream_t stream) {
+  const int BH = p.B * p.H;
+  const int n_qtiles = (p.N + 32 * kBwdWaves - 1) / (32 * kBwdWaves);
+  const unsigned short* q = static_cast<const unsigned short*>(p.q);
+  const unsigned short* k = static_cast<const unsigned short*>(p.k);
+  const unsigned short* v = static_cast<const unsigned short*>(p.v);
+  const unsigned short* dout = static_cast<const unsigned short*>(p.dout);
+  float* dws = static_cast<float*>(p.workspace);
+  hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)((int64_t)n_qtiles * BH)),
+                     dim3(kBwdThreads), 0, stream, q, k, v,
+                     static_cast<const unsigned short*>(p.o), dout, p.lse,
+                     static_cast<unsigned short*>(p.dq), dws, p.N, BH, n_qtiles, p.scale);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)((int64_t)n_qtiles * BH)),
+                     dim3(kBwdThreads), 0, stream, q, k, v, dout, p.lse, dws,
+                     static_cast<unsigned short*>(p.dk), static_cast<unsigned short*>(p.dv), p.N, BH,
+                     p.scale);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_bwd_bf16(const BwdProblem& p, hipStream_t stream) {
+  if (p.d == 64) return p.causal ? launch_bwd<64, true>(p, stream) : launch_bwd<64, false>(p, stream);
+  return p.causal ? launch_bwd<128, true>(p, stream) : launch_bwd<128, false>(p, stream);
+}
+
+}  // namespace fa

@@ -35,6 +35,29 @@ struct GqaProblem {
   void* workspace;
 };
 
+// Backward problem (square, bf16): gradients dq, dk, dv of O = softmax(scale
+// Q K^T) V for the upstream gradient dout, from the forward's o and lse;
+// `workspace` holds the per-row D = <dO, O> (fp32 [B*H*N]).
+struct BwdProblem {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;
+  void* dq;
+  void* dk;
+  void* dv;
+  int B, H, N, d;
+  float scale;
+  int causal;
+  void* workspace;
+};
+
+inline int64_t bwd_workspace_bytes(int B, int H, int N) {
+  return ((int64_t)B * H * N * 4 + 255) / 256 * 256;
+}
+
 // Query rows per workgroup tile of the bf16 kernel.
 constexpr int kTileRows = 128;
 
@@ -77,5 +100,6 @@ inline SplitLayout splitkv_layout(int B, int H, int Nq, int d, int splits) {
 // the launch (hipSuccess or the runtime's error).
 hipError_t launch_fwd_f32(const Problem& p, hipStream_t stream);
 hipError_t launch_fwd_bf16(const GqaProblem& p, hipStream_t stream);
+hipError_t launch_bwd_bf16(const BwdProblem& p, hipStream_t stream);
 
 }  // namespace fa

@@ -179,3 +179,39 @@ def test_gqa_split_choice():
     # bad arguments give 1
     assert fa.fa_fwd_gqa_num_splits(1, 6, 4, 1, 100, 0, 256) == 1
     assert fa.fa_fwd_gqa_num_splits(0, 6, 3, 1, 100, 0, 256) == 1
+
+
+def _bwd_call(**kw):
+    args = dict(q=A, k=A + 8 * MB, v=A + 16 * MB, o=A + 24 * MB, dout=A + 32 * MB,
+                lse=A + 40 * MB, dq=A + 48 * MB, dk=A + 56 * MB, dv=A + 64 * MB,
+                B=1, H=2, N=64, d=64, scale=0.125, causal=0, ws=A + 72 * MB, ws_bytes=1 << 20,
+                stream=None)
+    args.update(kw)
+    return fa.fa_bwd(args["q"], args["k"], args["v"], args["o"], args["dout"], args["lse"],
+                     args["dq"], args["dk"], args["dv"], args["B"], args["H"], args["N"], args["d"],
+                     args["scale"], args["causal"], args["ws"], args["ws_bytes"], args["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), fa.FA_ERR_NULL), (dict(o=None), fa.FA_ERR_NULL),
+    (dict(dout=None), fa.FA_ERR_NULL), (dict(lse=None), fa.FA_ERR_NULL),
+    (dict(dq=None), fa.FA_ERR_NULL), (dict(dv=None), fa.FA_ERR_NULL),
+    (dict(B=0), fa.FA_ERR_SHAPE), (dict(N=0), fa.FA_ERR_SHAPE),
+    (dict(N=1 << 23, d=128), fa.FA_ERR_SHAPE),
+    (dict(d=96), fa.FA_ERR_UNSUPPORTED_D), (dict(scale=float("nan")), fa.FA_ERR_SCALE),
+    (dict(causal=5), fa.FA_ERR_CAUSAL),
+    (dict(dk=A + 56 * MB + 2), fa.FA_ERR_ALIGN), (dict(ws=A + 72 * MB + 8), fa.FA_ERR_ALIGN),
+    (dict(ws=None), fa.FA_ERR_WORKSPACE), (dict(ws_bytes=16), fa.FA_ERR_WORKSPACE),
+    (dict(dq=A), fa.FA_ERR_ALIAS), (dict(dk=A + 48 * MB), fa.FA_ERR_ALIAS),
+    (dict(dv=A + 40 * MB), fa.FA_ERR_ALIAS), (dict(ws=A + 64 * MB), fa.FA_ERR_ALIAS),
+    (dict(dq=A + 32 * MB + 64), fa.FA_ERR_ALIAS),
+])
+def test_bwd_bad_arguments_rejected_on_host(kw, status):
+    assert _bwd_call(**kw) == status
+
+
+def test_bwd_workspace_size():
+    assert fa.fa_bwd_workspace_size(2, 8, 1024, 64) == 2 * 8 * 1024 * 4
+    assert fa.fa_bwd_workspace_size(1, 1, 3, 128) == 256
+    assert fa.fa_bwd_workspace_size(1, 1, 3, 80) == 0
+    assert fa.fa_bwd_workspace_size(0, 1, 3, 64) == 0

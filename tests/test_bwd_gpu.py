@@ -1,0 +1,100 @@
+"""Parity of the attention backward (fa_bwd) with the fp64 oracle.
+
+Every case runs the forward pass on the GPU (fa_fwd) for O and LSE, then
+fa_bwd, and compares dQ, dK and dV with the oracle's gradients of the same
+bf16 inputs.  Bound, per gradient: max |dX - dX_ref| <= 2e-2 * max |dX_ref|
+(the bf16 bound of the forward's O: inputs, probabilities and dS are rounded
+to bf16 for the products, accumulation is fp32).
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from io_aware_softmax_fwd_amd import workloads as W
+
+from gpu_util import note, torch_or_skip, upload
+
+pytestmark = pytest.mark.gpu
+
+BWD_TOL = 2e-2
+
+
+def _bf(shape, seed, scale=1.0):
+    x = np.random.default_rng(seed).standard_normal(shape, dtype=np.float32) * scale
+    return W.bf16_bits_to_f32(W.bf16_bits_rne(x))
+
+
+def _run(q, k, v, g, scale, causal):
+    torch = torch_or_skip()
+    import io_aware_softmax_fwd_amd as fa
+    qd, kd, vd, gd = (upload(x, "bf16") for x in (q, k, v, g))
+    o, lse = fa.fwd(qd, kd, vd, scale=scale, causal=causal)
+    dq, dk, dv = fa.bwd(qd, kd, vd, o, lse, gd, scale=scale, causal=causal)
+    torch.cuda.synchronize()
+    return [t.float().cpu().numpy().astype(np.float64) for t in (dq, dk, dv)]
+
+
+def _check(got, ref, what):
+    for name, a, b in zip(("dQ", "dK", "dV"), got, ref):
+        assert np.all(np.isfinite(a)), "%s %s: non-finite" % (what, name)
+        err, mx = float(np.abs(a - b).max()), float(np.abs(b).max())
+        note("%s %s: max|err|=%.3e  max|ref|=%.3e  ratio=%.2e" % (what, name, err, mx, err / max(mx, 1e-30)))
+        assert err <= BWD_TOL * mx, "%s %s: %.3e > %.3e" % (what, name, err, BWD_TOL * mx)
+
+
+CASES = [
+    # (B, H, N, d, causal)
+    (1, 2, 64, 64, False),
+    (1, 2, 64, 64, True),
+    (2, 3, 200, 64, True),
+    (1, 2, 257, 128, True),
+    (1, 1, 1, 128, True),
+    (1, 1, 1, 64, False),
+    (1, 2, 130, 128, False),
+    (2, 2, 333, 64, False),
+    (1, 1, 500, 128, True),
+    (1, 1, 1000, 128, False),
+]
+
+
+@pytest.mark.parametrize("B,H,N,d,causal", CASES)
+def test_bwd_matches_oracle(B, H, N, d, causal):
+    case = "bwd B=%d H=%d N=%d d=%d causal=%d" % (B, H, N, d, causal)
+    note(case)
+    seed = 5 * N + d + 7 * H + causal
+    q, k, v, g = (_bf((B, H, N, d), seed + t) for t in range(4))
+    scale = float(np.float32(1 / math.sqrt(d)))
+    got = _run(q, k, v, g, scale, causal)
+    ref = oracle.attention_bwd_c(q, k, v, g, scale, causal)
+    _check(got, ref, case)
+
+
+def test_bwd_deterministic():
+    """No atomics: two launches give identical bits."""
+    torch = torch_or_skip()
+    import io_aware_softmax_fwd_amd as fa
+    q, k, v, g = (upload(_bf((2, 4, 300, 128), 90 + t), "bf16") for t in range(4))
+    o, lse = fa.fwd(q, k, v, causal=True)
+    a = fa.bwd(q, k, v, o, lse, g, causal=True)
+    b = fa.bwd(q, k, v, o, lse, g, causal=True)
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+@pytest.mark.parametrize("cfg,heads", [(2, None), (3, [0, 63]), (4, [5]), (5, [2])])
+def test_bwd_workload_shapes(cfg, heads):
+    """The forward workloads' shapes and input recipes (dO drawn N(0,1) with
+    seed 1000*cfg + 6); the larger ones are checked on the listed heads."""
+    torch_or_skip()
+    w = W.WORKLOADS[cfg]
+    note("bwd workload C%d: %s heads=%s" % (cfg, w.describe(), heads))
+    x = W.make_inputs(w)
+    g = _bf((w.B, w.H, w.N, w.d), 1000 * cfg + 6)
+    got = _run(x["q"], x["k"], x["v"], g, w.scale, w.causal)
+    ref = oracle.attention_bwd_c(x["q"], x["k"], x["v"], g, w.scale, w.causal, heads=heads)
+    if heads is not None:
+        got = [a.reshape(w.B * w.H, w.N, w.d)[heads] for a in got]
+    _check(got, ref, "C%d" % cfg)
