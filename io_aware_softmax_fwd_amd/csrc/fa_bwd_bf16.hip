@@ -344,10 +344,13 @@ struct BwdKV {
     const unsigned char* gt = gbuf[PAR];
     const float* lt = lbuf[PAR];
     const float* dt = dbuf[PAR];
-#pragma unroll
+    // The two 32-query halves run as a loop, not unrolled: two copies in
+    // flight need more registers than one wave per SIMD has.  Halves wholly
+    // above the diagonal are still computed (their probabilities are 0);
+    // skipping them made the accumulators pass through a branch merge that
+    // the compiler could only serve by spilling.
+#pragma unroll 1
     for (int h2 = 0; h2 < 2; ++h2) {
-      // causal: every query of this half precedes every key of the wave
-      if (MASK && CAUSAL && q0 + 32 * h2 + 31 < kj - l32) continue;
       f32x16 s, dp;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -379,12 +382,13 @@ struct BwdKV {
           const int r = 8 * half + e;
           const float* Lr = reinterpret_cast<const float*>(&L[r >> 2]);
           const float* Dr = reinterpret_cast<const float*>(&Dd[r >> 2]);
-          float p0 = __builtin_amdgcn_exp2f(fmaf(s[r], c, -Lr[r & 3]));
-          float p1 = __builtin_amdgcn_exp2f(fmaf(s[r + 1], c, -Lr[(r + 1) & 3]));
+          float s0 = s[r], s1 = s[r + 1];
           if (MASK && CAUSAL) {
-            if ((r & 3) + 8 * (r >> 2) < qmin) p0 = 0.f;
-            if (((r + 1) & 3) + 8 * ((r + 1) >> 2) < qmin) p1 = 0.f;
+            if ((r & 3) + 8 * (r >> 2) < qmin) s0 = -INFINITY;
+            if (((r + 1) & 3) + 8 * ((r + 1) >> 2) < qmin) s1 = -INFINITY;
           }
+          const float p0 = __builtin_amdgcn_exp2f(fmaf(s0, c, -Lr[r & 3]));
+          const float p1 = __builtin_amdgcn_exp2f(fmaf(s1, c, -Lr[(r + 1) & 3]));
           wp[e / 2] = pack_bf16x2(p0, p1);
           wd[e / 2] = pack_bf16x2(p0 * (dp[r] - Dr[r & 3]), p1 * (dp[r + 1] - Dr[(r + 1) & 3]));
         }
