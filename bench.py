@@ -33,6 +33,11 @@ LSE from one fa_fwd call and dO drawn N(0,1) (seed 1000*cfg + 6); FLOPs are
 counted as 2.5x the forward's (five N^2 d products, causal halved; the
 kernels compute seven, recomputing S and dP for dQ).
 
+--fp8 times the fp8 forward (fa_fwd_fp8) of the workload, with Q, K and V
+quantized to the MX E4M3 block format beforehand (fa_quantize_qk_fp8,
+fa_quantize_v_fp8; their time is reported as quantize_ms, outside the
+step); FLOPs as for the bf16 forward, peak the dense fp8 matrix-core peak.
+
 --copy-bytes S runs only a plain device-to-device copy of S bytes (used to
 calibrate the FETCH_SIZE / WRITE_SIZE counters) and exits.
 
@@ -55,6 +60,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 matrix-core peak (published)
+PEAK_FP8_TFLOPS = 5000.0        # MI355X dense fp8 matrix-core peak (published)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fa_fwd_bf16_traffic.json")
 KERNEL_SOURCES = ["fa_fwd_bf16.hip", "fa_internal.h", "fa_api.cpp"]
 
@@ -341,6 +347,58 @@ def bwd_bench(fa, args, w, x):
                          "executed_flops": 3.5 * w.flops}}
 
 
+def fp8_bench(fa, args, w, x):
+    """Time fa_fwd_fp8 on the workload's quantized inputs; returns the JSON line."""
+    import torch
+    dev = torch.device("cuda:0")
+
+    def up(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    q, k, v = up(x["q_bits"]), up(x["k_bits"]), up(x["v_bits"])
+    stream = torch.cuda.current_stream(dev)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record(stream)
+    q8, qs = fa.quantize_qk_fp8(q)
+    k8, ks = fa.quantize_qk_fp8(k)
+    v8t, vs = fa.quantize_v_fp8(v)
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    quant_ms = ev[0].elapsed_time(ev[1])
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+    a = (q8.data_ptr(), qs.data_ptr(), k8.data_ptr(), ks.data_ptr(), v8t.data_ptr(), vs.data_ptr(),
+         o.data_ptr(), lse.data_ptr(), w.B, w.H, w.N, w.d, w.scale, int(w.causal), stream.cuda_stream)
+    for _ in range(args.warmup):
+        st = fa.fa_fwd_fp8(*a)
+        if st != 0:
+            raise fa.FaError(st, "fa_fwd_fp8")
+    torch.cuda.synchronize()
+    if not (torch.isfinite(lse).all() and torch.isfinite(o.float()).all()):
+        raise RuntimeError("non-finite output")
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        fa.fa_fwd_fp8(*a)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = ev0.elapsed_time(ev1) / args.steps
+    ach = w.flops / (ms * 1e-3) / 1e12
+    return {"metric": "fp8 fwd attention TFLOP/s (4BHN^2d, causal halved), MX E4M3 inputs resident",
+            "value": round(w.flops / (wall / args.steps) / 1e12, 2), "unit": "TFLOP/s", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall * 1e3 / args.steps, 4),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp8_e4m3",
+            "data": "synthetic (seeded N(0,1) draws, bf16-rounded, then MX E4M3 block-quantized)",
+            "config": {"workload": w.name + "_fp8", "B": w.B, "H": w.H, "N": w.N, "d": w.d,
+                       "causal": w.causal, "flops": w.flops, "entry_point": "fa_fwd_fp8",
+                       "quantize_ms": round(quant_ms, 4)},
+            "roofline": {"bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_FP8_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(ach / PEAK_FP8_TFLOPS, 4), "traffic": None,
+                         "kernel_ms": round(ms, 4)}}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -354,6 +412,7 @@ def main():
     ap.add_argument("--decode", type=int, default=0, metavar="NK")
     ap.add_argument("--hkv", type=int, default=0, metavar="HKV")
     ap.add_argument("--bwd", action="store_true")
+    ap.add_argument("--fp8", action="store_true")
     args = ap.parse_args()
 
     if args.summarize:
@@ -388,6 +447,11 @@ def main():
         if w.dtype != "bf16":
             raise SystemExit("--bwd needs a bf16 workload")
         print(json.dumps(bwd_bench(fa, args, w, x)), flush=True)
+        return
+    if args.fp8:
+        if w.dtype != "bf16":
+            raise SystemExit("--fp8 needs a bf16 workload")
+        print(json.dumps(fp8_bench(fa, args, w, x)), flush=True)
         return
     hkv = args.hkv or w.H
     if args.hkv:

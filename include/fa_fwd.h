@@ -33,6 +33,7 @@
 #define FA_FWD_H
 
 #include <stddef.h>
+#include <stdint.h>
 #include <hip/hip_runtime_api.h>
 
 #ifdef __cplusplus
@@ -183,6 +184,50 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
 /* Bytes of workspace fa_bwd needs (0 if an argument is out of range).
  * Host only, no HIP call. */
 size_t fa_bwd_workspace_size(int B, int H, int N, int d);
+
+/*
+ * fp8 forward with per-block scales: the low-precision variant of the method
+ * (zzszmyf.github.io notes "FlashAttention 原理是什么", section 10 item ③ and
+ * section 12.2: block-wise quantization with one scale per block).  Inputs
+ * are quantized to OCP E4M3 codes in the MX block layout that gfx950's
+ * matrix cores consume: every 32 consecutive elements along a contracted
+ * dimension share one E8M0 scale byte E (value 2^(E-127)).  For a block with
+ * largest magnitude amax = m * 2^f (1 <= m < 2) the scale exponent is
+ * X = f - 8 if m <= 1.75 else f - 7 (the smallest X with amax <= 448 * 2^X),
+ * E = clamp(X + 127, 0, 254) (E = 0 for a zero or subnormal amax), and each
+ * code is the round-to-nearest-even E4M3 value of x * 2^(127 - E); nothing
+ * is clipped.  The dequantized input is decode(code) * 2^(E - 127).
+ *
+ * fa_quantize_qk_fp8: Q or K rows.  x bf16 [rows, d] (device) -> x8 codes
+ *   [rows, d] (one byte each) and xs scales [rows, d/32] (block c covers
+ *   dims 32c .. 32c+31).  rows >= 1, d in {64, 128}.
+ * fa_quantize_v_fp8: V of BH = B*H heads.  v bf16 [BH, N, d] -> v8t codes in
+ *   fa_fp8_v_bytes(BH, N, d) bytes and vs scales in
+ *   fa_fp8_v_scale_bytes(BH, N, d) bytes.  Blocks are 32 consecutive keys of
+ *   one head dim.  Layout: T = ceil(N/64) tiles of 64 keys per head; v8t is
+ *   [BH, T, d, 64] (each tile transposed, keys past N zero) with position
+ *   32h + j (h in {0,1}, j in 0..31) of a tile row holding key
+ *   32*(j/16) + (j%4) + 8*((j%16)/4) + 4h of the tile; vs is [BH, T, 2, 32,
+ *   d/32], element (t, b, i, c) the scale of keys 64t + 32b .. +31 of head
+ *   dim 32c + i.
+ * fa_fwd_fp8: attention of the dequantized inputs.  q8, qs, k8, ks as
+ *   written by fa_quantize_qk_fp8 for the [B*H*N, d] rows of Q and K; v8t,
+ *   vs by fa_quantize_v_fp8 for V; o bf16 [B,H,N,d] and lse fp32 [B,H,N]
+ *   written as by fa_fwd (same scale and causal arguments).  Scores and the
+ *   products with V run on fp8 matrix cores with fp32 accumulation; the
+ *   softmax is fp32 and the probabilities are rounded to E4M3 (values at
+ *   most 2^8) for the product with V, the row sums taken over the same
+ *   rounded values.
+ * All pointers are device pointers, 16-byte aligned; outputs must not overlap
+ * inputs.  Errors as for fa_fwd.  Each call queues one kernel on `stream`.
+ */
+int fa_quantize_qk_fp8(const void* x, int64_t rows, int d, void* x8, void* xs, hipStream_t stream);
+int fa_quantize_v_fp8(const void* v, int BH, int N, int d, void* v8t, void* vs, hipStream_t stream);
+size_t fa_fp8_v_bytes(int BH, int N, int d);        /* 0 if out of range; host only */
+size_t fa_fp8_v_scale_bytes(int BH, int N, int d);  /* 0 if out of range; host only */
+int fa_fwd_fp8(const void* q8, const void* qs, const void* k8, const void* ks, const void* v8t,
+               const void* vs, void* o, float* lse, int B, int H, int N, int d, float scale,
+               int causal, hipStream_t stream);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* fa_strerror(int status);

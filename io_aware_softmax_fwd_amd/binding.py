@@ -17,6 +17,11 @@ Low level (same names and arguments as the C functions, raw pointers):
     fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, scale, causal,
            workspace, workspace_bytes, stream)                 -> status
     fa_bwd_workspace_size(B, H, N, d)                          -> bytes
+    fa_quantize_qk_fp8(x, rows, d, x8, xs, stream)             -> status
+    fa_quantize_v_fp8(v, BH, N, d, v8t, vs, stream)            -> status
+    fa_fp8_v_bytes(BH, N, d), fa_fp8_v_scale_bytes(BH, N, d)   -> bytes
+    fa_fwd_fp8(q8, qs, k8, ks, v8t, vs, o, lse, B, H, N, d, scale, causal,
+               stream)                                         -> status
     fa_strerror(status)                                        -> str
 High level (torch tensors on a ROCm device):
     fwd(q, k, v, scale=None, causal=False, out=None, lse=None) -> (o, lse)
@@ -26,6 +31,10 @@ High level (torch tensors on a ROCm device):
             workspace=None)                                    -> (o, lse)
     bwd(q, k, v, o, lse, dout, scale=None, causal=False,
         workspace=None)                                        -> (dq, dk, dv)
+    quantize_qk_fp8(x)                                         -> (x8, xs)
+    quantize_v_fp8(v)                                          -> (v8t, vs)
+    fwd_fp8(q8, qs, k8, ks, v8t, vs, shape, scale=None,
+            causal=False)                                      -> (o, lse)
 """
 import ctypes
 import math
@@ -48,7 +57,8 @@ FA_ERR_HEADS = 11
 
 EXPORTED = ("fa_fwd", "fa_fwd_f32", "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_size",
             "fa_fwd_splitkv_num_splits", "fa_fwd_gqa", "fa_fwd_gqa_num_splits", "fa_bwd",
-            "fa_bwd_workspace_size", "fa_strerror")
+            "fa_bwd_workspace_size", "fa_quantize_qk_fp8", "fa_quantize_v_fp8", "fa_fp8_v_bytes",
+            "fa_fp8_v_scale_bytes", "fa_fwd_fp8", "fa_strerror")
 
 _lib = None
 
@@ -94,6 +104,19 @@ def load():
                             ctypes.c_void_p])
     lib.fa_bwd_workspace_size.restype = ctypes.c_size_t
     lib.fa_bwd_workspace_size.argtypes = [ctypes.c_int] * 4
+    lib.fa_quantize_qk_fp8.restype = ctypes.c_int
+    lib.fa_quantize_qk_fp8.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p,
+                                       ctypes.c_void_p, ctypes.c_void_p]
+    lib.fa_quantize_v_fp8.restype = ctypes.c_int
+    lib.fa_quantize_v_fp8.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                      ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    for name in ("fa_fp8_v_bytes", "fa_fp8_v_scale_bytes"):
+        f = getattr(lib, name)
+        f.restype = ctypes.c_size_t
+        f.argtypes = [ctypes.c_int] * 3
+    lib.fa_fwd_fp8.restype = ctypes.c_int
+    lib.fa_fwd_fp8.argtypes = ([ctypes.c_void_p] * 8 + [ctypes.c_int] * 4 +
+                               [ctypes.c_float, ctypes.c_int, ctypes.c_void_p])
     lib.fa_strerror.restype = ctypes.c_char_p
     lib.fa_strerror.argtypes = [ctypes.c_int]
     _lib = lib
@@ -140,6 +163,26 @@ def fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, scale, causal, workspa
 
 def fa_bwd_workspace_size(B, H, N, d):
     return int(load().fa_bwd_workspace_size(B, H, N, d))
+
+
+def fa_quantize_qk_fp8(x, rows, d, x8, xs, stream):
+    return load().fa_quantize_qk_fp8(x, rows, d, x8, xs, stream)
+
+
+def fa_quantize_v_fp8(v, BH, N, d, v8t, vs, stream):
+    return load().fa_quantize_v_fp8(v, BH, N, d, v8t, vs, stream)
+
+
+def fa_fp8_v_bytes(BH, N, d):
+    return int(load().fa_fp8_v_bytes(BH, N, d))
+
+
+def fa_fp8_v_scale_bytes(BH, N, d):
+    return int(load().fa_fp8_v_scale_bytes(BH, N, d))
+
+
+def fa_fwd_fp8(q8, qs, k8, ks, v8t, vs, o, lse, B, H, N, d, scale, causal, stream):
+    return load().fa_fwd_fp8(q8, qs, k8, ks, v8t, vs, o, lse, B, H, N, d, scale, causal, stream)
 
 
 def fa_strerror(status):
@@ -305,3 +348,64 @@ def bwd(q, k, v, o, lse, dout, scale=None, causal=False, workspace=None, stream=
     if st != FA_OK:
         raise FaError(st, "fa_bwd")
     return dq, dk, dv
+
+
+def _bf16_4d(name, t):
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.device.type != "cuda" or not t.is_contiguous() or t.dim() != 4 or t.dtype != torch.bfloat16:
+        raise ValueError("%s must be a contiguous 4-D bf16 GPU tensor" % name)
+
+
+def quantize_qk_fp8(x, stream=None):
+    """MX fp8 quantization of a bf16 [B,H,N,d] Q or K: returns (codes uint8
+    [B,H,N,d], E8M0 scales uint8 [B,H,N,d/32])."""
+    import torch
+    _bf16_4d("x", x)
+    B, H, N, d = x.shape
+    x8 = torch.empty((B, H, N, d), dtype=torch.uint8, device=x.device)
+    xs = torch.empty((B, H, N, d // 32), dtype=torch.uint8, device=x.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device).cuda_stream
+    st = fa_quantize_qk_fp8(x.data_ptr(), B * H * N, d, x8.data_ptr(), xs.data_ptr(), stream)
+    if st != FA_OK:
+        raise FaError(st, "fa_quantize_qk_fp8")
+    return x8, xs
+
+
+def quantize_v_fp8(v, stream=None):
+    """MX fp8 quantization of a bf16 [B,H,N,d] V into the transposed tile
+    layout: returns (codes uint8, scales uint8), flat buffers of
+    fa_fp8_v_bytes / fa_fp8_v_scale_bytes bytes."""
+    import torch
+    _bf16_4d("v", v)
+    B, H, N, d = v.shape
+    v8t = torch.empty(fa_fp8_v_bytes(B * H, N, d), dtype=torch.uint8, device=v.device)
+    vs = torch.empty(fa_fp8_v_scale_bytes(B * H, N, d), dtype=torch.uint8, device=v.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(v.device).cuda_stream
+    st = fa_quantize_v_fp8(v.data_ptr(), B * H, N, d, v8t.data_ptr(), vs.data_ptr(), stream)
+    if st != FA_OK:
+        raise FaError(st, "fa_quantize_v_fp8")
+    return v8t, vs
+
+
+def fwd_fp8(q8, qs, k8, ks, v8t, vs, scale=None, causal=False, stream=None):
+    """fp8 attention forward of quantized inputs (as returned by
+    quantize_qk_fp8 and quantize_v_fp8); q8 gives the [B,H,N,d] shape.
+    Returns (o bf16 [B,H,N,d], lse fp32 [B,H,N])."""
+    import torch
+    B, H, N, d = q8.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    o = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=q8.device)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q8.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q8.device).cuda_stream
+    st = fa_fwd_fp8(q8.data_ptr(), qs.data_ptr(), k8.data_ptr(), ks.data_ptr(), v8t.data_ptr(),
+                    vs.data_ptr(), o.data_ptr(), lse.data_ptr(), B, H, N, d, float(scale),
+                    int(bool(causal)), stream)
+    if st != FA_OK:
+        raise FaError(st, "fa_fwd_fp8")
+    return o, lse

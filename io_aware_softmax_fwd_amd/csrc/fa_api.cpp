@@ -7,6 +7,8 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <initializer_list>
+#include <utility>
 
 #include "fa_fwd.h"
 #include "fa_internal.h"
@@ -126,6 +128,18 @@ int validate_bwd(const void* q, const void* k, const void* v, const void* o, con
   return FA_OK;
 }
 
+bool any_misaligned(std::initializer_list<const void*> ps) {
+  for (const void* p : ps)
+    if (misaligned(p)) return true;
+  return false;
+}
+
+bool any_overlap(const void* out, int64_t out_bytes, std::initializer_list<std::pair<const void*, int64_t>> ins) {
+  for (const auto& in : ins)
+    if (overlap(out, out_bytes, in.first, in.second)) return true;
+  return false;
+}
+
 }  // namespace
 
 extern "C" {
@@ -200,6 +214,58 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
   if (st != FA_OK) return st;
   const fa::BwdProblem p{q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, scale, causal, workspace};
   return fa::launch_bwd_bf16(p, stream) == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+int fa_quantize_qk_fp8(const void* x, int64_t rows, int d, void* x8, void* xs, hipStream_t stream) {
+  if (!x || !x8 || !xs) return FA_ERR_NULL;
+  if (rows < 1) return FA_ERR_SHAPE;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED_D;
+  if (rows * d >= kMaxElems) return FA_ERR_SHAPE;
+  if (any_misaligned({x, x8, xs})) return FA_ERR_ALIGN;
+  const int64_t xb = rows * d * 2, cb = rows * d, sb = rows * (d / 32);
+  if (any_overlap(x8, cb, {{x, xb}, {xs, sb}}) || any_overlap(xs, sb, {{x, xb}})) return FA_ERR_ALIAS;
+  return fa::launch_quantize_qk_fp8(x, rows, d, x8, xs, stream) == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+size_t fa_fp8_v_bytes(int BH, int N, int d) {
+  if (BH < 1 || N < 1 || (d != 64 && d != 128)) return 0;
+  return (size_t)fa::fp8_v_code_bytes(BH, N, d);
+}
+
+size_t fa_fp8_v_scale_bytes(int BH, int N, int d) {
+  if (BH < 1 || N < 1 || (d != 64 && d != 128)) return 0;
+  return (size_t)fa::fp8_v_scale_bytes(BH, N, d);
+}
+
+int fa_quantize_v_fp8(const void* v, int BH, int N, int d, void* v8t, void* vs, hipStream_t stream) {
+  if (!v || !v8t || !vs) return FA_ERR_NULL;
+  if (BH < 1 || N < 1) return FA_ERR_SHAPE;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED_D;
+  if ((int64_t)BH * N * d >= kMaxElems || (int64_t)N * d * 2 >= (int64_t(1) << 31)) return FA_ERR_SHAPE;
+  if (any_misaligned({v, v8t, vs})) return FA_ERR_ALIGN;
+  const int64_t vb = (int64_t)BH * N * d * 2, cb = fa::fp8_v_code_bytes(BH, N, d),
+                sb = fa::fp8_v_scale_bytes(BH, N, d);
+  if (any_overlap(v8t, cb, {{v, vb}, {vs, sb}}) || any_overlap(vs, sb, {{v, vb}})) return FA_ERR_ALIAS;
+  return fa::launch_quantize_v_fp8(v, BH, N, d, v8t, vs, stream) == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+int fa_fwd_fp8(const void* q8, const void* qs, const void* k8, const void* ks, const void* v8t, const void* vs,
+               void* o, float* lse, int B, int H, int N, int d, float scale, int causal, hipStream_t stream) {
+  if (!q8 || !qs || !k8 || !ks || !v8t || !vs || !o || !lse) return FA_ERR_NULL;
+  if (B < 1 || H < 1 || N < 1) return FA_ERR_SHAPE;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED_D;
+  const int64_t rows = (int64_t)B * H * N;
+  if (rows * d >= kMaxElems || (int64_t)N * d * 2 >= (int64_t(1) << 31)) return FA_ERR_SHAPE;
+  if (!(scale > 0.f) || !isfinite(scale)) return FA_ERR_SCALE;
+  if (causal != 0 && causal != 1) return FA_ERR_CAUSAL;
+  if (any_misaligned({q8, qs, k8, ks, v8t, vs, o, lse})) return FA_ERR_ALIGN;
+  const int64_t cb = rows * d, sb = rows * (d / 32), ob = rows * d * 2, lb = rows * 4,
+                vcb = fa::fp8_v_code_bytes((int64_t)B * H, N, d), vsb = fa::fp8_v_scale_bytes((int64_t)B * H, N, d);
+  const std::initializer_list<std::pair<const void*, int64_t>> ins = {
+      {q8, cb}, {qs, sb}, {k8, cb}, {ks, sb}, {v8t, vcb}, {vs, vsb}};
+  if (any_overlap(o, ob, ins) || any_overlap(lse, lb, ins) || overlap(o, ob, lse, lb)) return FA_ERR_ALIAS;
+  const fa::Fp8Problem p{q8, qs, k8, ks, v8t, vs, o, lse, B, H, N, d, scale, causal};
+  return fa::launch_fwd_fp8(p, stream) == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
 const char* fa_strerror(int status) {

@@ -1,0 +1,490 @@
+// fp8 attention forward with per-block scales on the gfx950 matrix cores.
+//
+// The low-precision variant quantizes Q, K and V block by block, each block
+// with its own scale (zzszmyf.github.io notes "FlashAttention 原理是什么",
+// section 10 item ③ and section 12.2).  Blocks here are the 32-element
+// blocks of the MX layout that v_mfma_scale_f32_32x32x64_f8f6f4 consumes:
+// E4M3 codes plus one E8M0 power-of-two scale per 32 consecutive elements of
+// the contracted dimension, applied by the matrix core itself.
+//   Q, K : blocks of 32 consecutive head dims of one row (S = Q K^T contracts
+//          over dims).  x8 [rows, d] codes, xs [rows, d/32] scales.
+//   V    : blocks of 32 consecutive keys of one head dim (O = P V contracts
+//          over keys), stored per 64-key tile transposed as v8t
+//          [B*H, T, d, 64] (T = ceil(N/64), keys past N are zero) with the
+//          keys of a tile in the order the score accumulators hand them to
+//          the P operand: position 32*h + j of a row holds key
+//          32*(j/16) + (j%4) + 8*((j%16)/4) + 4*h (h = 0, 1; j = 0..31).
+//          vs [B*H, T, 2, 32, d/32]: element (t, b, i, c) scales keys
+//          64t + 32b .. +31 of head dim 32c + i.
+// Scale rule of a block with largest magnitude amax = m * 2^f (1 <= m < 2):
+// X = f - 8 if m <= 1.75 else f - 7 (the smallest X with amax <= 448 * 2^X),
+// E = clamp(X + 127, 0, 254), 0 for a zero or subnormal amax; codes are the
+// round-to-nearest-even E4M3 values of x * 2^(127 - E).
+//
+// The attention kernel follows the bf16 one (transposed products, online
+// softmax with a lazy offset, K/V tiles streamed by LDS-DMA, two buffers):
+//   S^T = K Q^T      v_mfma_scale 32x32x64, K codes from LDS (A), Q codes in
+//                    registers (B), their block scales applied by the MFMA;
+//   P = exp2(...)    fp32, rounded to E4M3 (values <= 2^8 by the lazy
+//                    threshold, so no scale is needed: E8M0 127);
+//   l               a ones-operand MFMA over the same rounded P, so the
+//                    denominator sees exactly the numerator's weights;
+//   O^T += V^T P^T   v_mfma_scale 32x32x64 with the V block scales.
+// The fp8 matrix cores run at twice the bf16 rate, so a 64-key tile costs
+// nine 32x32x64 products per wave against thirty-two 32x32x16 in bf16.
+#include <math.h>
+
+#include "fa_device.h"
+#include "fa_internal.h"
+
+namespace fa {
+namespace {
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+constexpr int kF8Waves = 4;
+constexpr int kF8Threads = 64 * kF8Waves;
+constexpr int kF8Keys = 64;              // keys per K/V tile
+constexpr float kF8Lazy = 8.0f;          // log2 headroom before a rescale
+constexpr int kUnitScale = 0x7F7F7F7F;   // E8M0 127 = 2^0 in every byte
+
+// Scale rule of one block from the float32 bit pattern of its largest
+// magnitude: E8M0 exponent E (see the file comment).
+__device__ __forceinline__ int mx_scale_exponent(unsigned amax_bits) {
+  const int field = (amax_bits >> 23) & 0xFF;
+  if (field == 0) return 0;
+  const int e = field - 8 + ((amax_bits & 0x7FFFFF) > 0x600000 ? 1 : 0);
+  return min(max(e, 0), 254);
+}
+
+// x * 2^(127 - E), clamped to the E4M3 range (never binding for finite x),
+// two values packed to E4M3 by round to nearest even into bytes 0-1 or 2-3.
+__device__ __forceinline__ float mx_scaled(float x, int E) {
+  return fminf(fmaxf(__builtin_ldexpf(x, 127 - E), -448.f), 448.f);
+}
+
+__device__ __forceinline__ float bf16_to_f32(unsigned short b) { return __uint_as_float((unsigned)b << 16); }
+
+// ------------------------------------------------------------ quantizers
+// One thread per 32-element block of a row (Q or K).
+template <int D>
+__global__ __launch_bounds__(256) void quant_rows_kernel(const unsigned short* __restrict__ x, int64_t rows,
+                                                        unsigned char* __restrict__ x8,
+                                                        unsigned char* __restrict__ xs) {
+  constexpr int NB = D / 32;
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= rows * NB) return;
+  const unsigned short* src = x + t * 32;
+  u32x4 raw[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) raw[i] = reinterpret_cast<const u32x4*>(src)[i];
+  const unsigned short* h = reinterpret_cast<const unsigned short*>(raw);
+  unsigned amax = 0;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) amax = max(amax, ((unsigned)h[i] << 16) & 0x7FFFFFFFu);
+  const int E = mx_scale_exponent(amax);
+  u32x4 out[2];
+#pragma unroll
+  for (int w = 0; w < 8; ++w) {
+    int word = 0;
+    word = __builtin_amdgcn_cvt_pk_fp8_f32(mx_scaled(bf16_to_f32(h[4 * w]), E),
+                                           mx_scaled(bf16_to_f32(h[4 * w + 1]), E), word, false);
+    word = __builtin_amdgcn_cvt_pk_fp8_f32(mx_scaled(bf16_to_f32(h[4 * w + 2]), E),
+                                           mx_scaled(bf16_to_f32(h[4 * w + 3]), E), word, true);
+    out[w / 4][w % 4] = (unsigned)word;
+  }
+  u32x4* dst = reinterpret_cast<u32x4*>(x8 + t * 32);
+  dst[0] = out[0];
+  dst[1] = out[1];
+  xs[t] = (unsigned char)E;
+}
+
+// One thread per (head, tile, key block b, head dim c): the 32 keys
+// 64t + 32b .. +31 of dim c.  Their codes go to two 16-byte runs of tile row
+// c: positions 16b .. 16b+15 (keys with bit 2 of the key index clear) and
+// 32 + 16b .. (bit 2 set), in the accumulator key order.
+template <int D>
+__global__ __launch_bounds__(256) void quant_v_kernel(const unsigned short* __restrict__ v, int BH, int N,
+                                                     int T, unsigned char* __restrict__ v8t,
+                                                     unsigned char* __restrict__ vs) {
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= (int64_t)BH * T * 2 * D) return;
+  const int c = (int)(t % D);
+  const int b = (int)((t / D) % 2);
+  const int64_t tile = t / (2 * D);            // bh * T + tile index
+  const int bh = (int)(tile / T);
+  const int k0 = (int)(tile % T) * kF8Keys + 32 * b;
+  const unsigned short* col = v + ((int64_t)bh * N) * D + c;
+  float val[32];
+  unsigned amax = 0;
+#pragma unroll
+  for (int r = 0; r < 32; ++r) {
+    const int key = k0 + r;
+    const unsigned short bits = key < N ? col[(int64_t)key * D] : (unsigned short)0;
+    val[r] = bf16_to_f32(bits);
+    amax = max(amax, ((unsigned)bits << 16) & 0x7FFFFFFFu);
+  }
+  const int E = mx_scale_exponent(amax);
+  // key r of the block (0..31): half h = (r/4)%2, slot j' = (r%4) + 4*(r/8)
+  u32x4 run[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      // slots j' = 4w .. 4w+3 of half h are keys r = 8w + 4h + 0..3
+      const int r0 = 8 * w + 4 * h;
+      int word = 0;
+      word = __builtin_amdgcn_cvt_pk_fp8_f32(mx_scaled(val[r0], E), mx_scaled(val[r0 + 1], E), word, false);
+      word = __builtin_amdgcn_cvt_pk_fp8_f32(mx_scaled(val[r0 + 2], E), mx_scaled(val[r0 + 3], E), word, true);
+      run[h][w] = (unsigned)word;
+    }
+  unsigned char* row = v8t + (tile * D + c) * kF8Keys;
+  *reinterpret_cast<u32x4*>(row + 16 * b) = run[0];
+  *reinterpret_cast<u32x4*>(row + 32 + 16 * b) = run[1];
+  vs[((tile * 2 + b) * 32 + (c % 32)) * (D / 32) + c / 32] = (unsigned char)E;
+}
+
+// ---------------------------------------------------------- attention
+template <int D> struct F8Cfg {
+  static constexpr int kStride = D + 16;               // bytes per K code row in LDS
+  static constexpr int vStride = 80;                   // bytes per V^T code row (64 + 16)
+  static constexpr int kTile = kF8Keys * kStride;      // 9 KB (d=128) or 5 KB (d=64)
+  static constexpr int vTile = D * vStride;            // 10 KB or 5 KB
+  static constexpr int kDma = kTile / 1024, vDma = vTile / 1024;
+  static constexpr int kDmaPerWave = (kDma + kF8Waves - 1) / kF8Waves;
+  static constexpr int vDmaPerWave = (vDma + kF8Waves - 1) / kF8Waves;
+  static_assert(kTile % 1024 == 0 && vTile % 1024 == 0, "tiles must be whole 1 KB blocks");
+};
+
+// Source offset (inside one tile) of LDS-DMA slot `slot` for LDS rows of
+// `stride` bytes holding `row_bytes` of data; pad slots re-fetch the last chunk.
+__device__ __forceinline__ int f8_dma_offset(int slot, int stride, int row_bytes) {
+  const int slots = stride / 16;
+  const int r = slot / slots;
+  const int cc = min(slot % slots, row_bytes / 16 - 1);
+  return r * row_bytes + 16 * cc;
+}
+
+template <int D, bool CAUSAL>
+struct FwdF8 {
+  static constexpr int KS = D / 64;          // 64-dim steps of S
+  static constexpr int DB = D / 32;          // 32-dim blocks of O
+  using C = F8Cfg<D>;
+
+  const unsigned char* kh;     // K codes of the head
+  const unsigned char* ksh;    // K scales of the head [N, D/32]
+  const unsigned char* vth;    // V^T tiles of the head
+  const unsigned char* vsh;    // V scales of the head
+  int N, wave, l32, hl, qw, qi;
+  float c, thr;
+  i32x8 qf[KS];                // Q codes of this lane's query (B operand)
+  int qsc;                     // byte ks: scale of Q block 2*ks + hl
+  f32x16 acc[DB];              // O^T
+  f32x16 lacc;                 // row sums (every element holds the lane's l)
+  float m;
+  int koff[C::kDmaPerWave], voff[C::vDmaPerWave];
+  int k_rd, v_rd;
+  unsigned ksw[2][2];          // K scale words of the key rows 32kb + l32, per buffer
+  unsigned vsw[2];             // V scale word (byte db) per buffer
+  unsigned char* kbuf[2];
+  unsigned char* vbuf[2];
+
+  // Queue tile k0 into buffer B: K and V^T codes by LDS-DMA, scale words
+  // into registers.
+  template <int B>
+  __device__ void issue(int k0) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    const __amdgpu_buffer_rsrc_t rk =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(kh + (int64_t)k0 * D), (short)0, (N - k0) * D, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(vth + (int64_t)(k0 / kF8Keys) * D * kF8Keys), (short)0, D * kF8Keys, 0x00020000);
+#pragma unroll
+    for (int i = 0; i < C::kDmaPerWave; ++i) {
+      const int blk = wave + kF8Waves * i;
+      if (C::kDma % kF8Waves == 0 || blk < C::kDma)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(kbuf[B] + blk * 1024), 16, koff[i], 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < C::vDmaPerWave; ++i) {
+      const int blk = wave + kF8Waves * i;
+      if (C::vDma % kF8Waves == 0 || blk < C::vDma)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(vbuf[B] + blk * 1024), 16, voff[i], 0, 0, 0);
+    }
+#endif
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const int key = k0 + 32 * kb + l32;
+      unsigned w = 0;
+      if (key < N) {
+        if constexpr (D == 128) w = *reinterpret_cast<const unsigned*>(ksh + (int64_t)key * 4);
+        else w = *reinterpret_cast<const unsigned short*>(ksh + (int64_t)key * 2);
+      }
+      ksw[B][kb] = w;
+    }
+    const int64_t vsrow = ((int64_t)(k0 / kF8Keys) * 2 + hl) * 32 + l32;
+    if constexpr (D == 128) vsw[B] = *reinterpret_cast<const unsigned*>(vsh + vsrow * 4);
+    else vsw[B] = *reinterpret_cast<const unsigned short*>(vsh + vsrow * 2);
+  }
+
+  template <bool MASK, int PAR>
+  __device__ void consume(int k0) {
+    const unsigned char* kt = kbuf[PAR] + k_rd;
+    const unsigned char* vt = vbuf[PAR] + v_rd;
+    f32x16 s[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
+      // scale word of this lane's key row: byte ks = block 2*ks + hl
+      const unsigned w = ksw[PAR][kb];
+      const unsigned ksc = D == 128 ? (((w >> (8 * hl)) & 0xFF) | (((w >> (16 + 8 * hl)) & 0xFF) << 8))
+                                    : ((w >> (8 * hl)) & 0xFF);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const unsigned char* src = kt + 32 * kb * C::kStride + 64 * ks;
+        const u32x4 a0 = *reinterpret_cast<const u32x4*>(src);
+        const u32x4 a1 = *reinterpret_cast<const u32x4*>(src + 32);
+        const i32x8 a = __builtin_bit_cast(i32x8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
+        if (ks == 0)
+          s[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, qf[ks], s[kb], 0, 0, 0, (int)ksc, 0, qsc);
+        else
+          s[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, qf[ks], s[kb], 0, 0, 1, (int)ksc, 1, qsc);
+      }
+    }
+    if constexpr (MASK) {
+      // key = k0 + 32*kb + (r&3) + 8*(r>>2) + 4*hl must be <= min(qi, N-1)
+      const int lim = (CAUSAL ? min(qi, N - 1) : N - 1) - k0 - 4 * hl;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (32 * kb + (r & 3) + 8 * (r >> 2) > lim) s[kb][r] = -INFINITY;
+    }
+    float mx = s[0][0];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = (kb == 0 ? 1 : 0); r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+    mx = max_across_halves(mx);
+    const bool upd = mx > m + thr;
+    if (__builtin_amdgcn_ballot_w64(upd)) {
+      asm volatile("" ::: "memory");   // keep this a taken/skipped branch
+      const float m_new = upd ? mx : m;
+      const float alpha = upd ? __builtin_amdgcn_exp2f((m - m_new) * c) : 1.f;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) lacc[r] *= alpha;
+      m = m_new;
+    }
+    const float mc = m * c;
+    // P rounded to E4M3: byte 16*kb + r of the operand holds element r of
+    // score block kb
+    i32x8 pf;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        int word = 0;
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kb][4 * w], c, -mc));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kb][4 * w + 1], c, -mc));
+        const float p2 = __builtin_amdgcn_exp2f(fmaf(s[kb][4 * w + 2], c, -mc));
+        const float p3 = __builtin_amdgcn_exp2f(fmaf(s[kb][4 * w + 3], c, -mc));
+        word = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, word, false);
+        word = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, word, true);
+        pf[4 * kb + w] = word;
+      }
+    const i32x8 ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838,
+                        0x38383838, 0x38383838, 0x38383838, 0x38383838};
+    lacc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones, pf, lacc, 0, 0, 0, kUnitScale, 0, kUnitScale);
+    const unsigned vsc = vsw[PAR];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const unsigned char* src = vt + 32 * db * C::vStride;
+      const u32x4 a0 = *reinterpret_cast<const u32x4*>(src);
+      const u32x4 a1 = *reinterpret_cast<const u32x4*>(src + 16);
+      const i32x8 a = __builtin_bit_cast(i32x8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
+      if (db == 0)
+        acc[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, pf, acc[db], 0, 0, 0, (int)vsc, 0, kUnitScale);
+      else if (db == 1)
+        acc[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, pf, acc[db], 0, 0, 1, (int)vsc, 0, kUnitScale);
+      else if (db == 2)
+        acc[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, pf, acc[db], 0, 0, 2, (int)vsc, 0, kUnitScale);
+      else
+        acc[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, pf, acc[db], 0, 0, 3, (int)vsc, 0, kUnitScale);
+    }
+  }
+
+  template <bool MASK, int PAR>
+  __device__ void step(int j, int t_end) {
+    const int k0 = j * kF8Keys;
+    if (j + 1 < t_end) issue<PAR ^ 1>(k0 + kF8Keys);
+    if (!MASK || !CAUSAL || k0 <= qw + 31) consume<MASK, PAR>(k0);
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+  }
+};
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kF8Threads, 2) void fwd_fp8_kernel(
+    const unsigned char* __restrict__ q8, const unsigned char* __restrict__ qs,
+    const unsigned char* __restrict__ k8, const unsigned char* __restrict__ ks,
+    const unsigned char* __restrict__ v8t, const unsigned char* __restrict__ vs,
+    unsigned short* __restrict__ o, float* __restrict__ lse, int N, int BH, int n_qtiles, float scale) {
+  using F = FwdF8<D, CAUSAL>;
+  using C = F8Cfg<D>;
+  __shared__ __attribute__((aligned(1024))) unsigned char k_lds0[C::kTile];
+  __shared__ __attribute__((aligned(1024))) unsigned char k_lds1[C::kTile];
+  __shared__ __attribute__((aligned(1024))) unsigned char v_lds0[C::vTile];
+  __shared__ __attribute__((aligned(1024))) unsigned char v_lds1[C::vTile];
+  constexpr int BR = 32 * kF8Waves;
+  const int T = (N + kF8Keys - 1) / kF8Keys;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int bh = blockIdx.x % BH;
+  const int qt = n_qtiles - 1 - blockIdx.x / BH;   // heaviest causal tiles first
+  const int q0 = qt * BR;
+
+  F f;
+  f.kbuf[0] = k_lds0;
+  f.kbuf[1] = k_lds1;
+  f.vbuf[0] = v_lds0;
+  f.vbuf[1] = v_lds1;
+  f.kh = k8 + (int64_t)bh * N * D;
+  f.ksh = ks + (int64_t)bh * N * (D / 32);
+  f.vth = v8t + (int64_t)bh * T * D * kF8Keys;
+  f.vsh = vs + (int64_t)bh * T * 2 * 32 * (D / 32);
+  f.N = N;
+  f.wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  f.l32 = lane & 31;
+  f.hl = lane >> 5;
+  f.qw = q0 + 32 * f.wave;
+  f.qi = f.qw + f.l32;
+  f.c = scale * kLog2e;
+  f.thr = kF8Lazy / f.c;
+  f.m = -INFINITY;
+#pragma unroll
+  for (int db = 0; db < F::DB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) f.acc[db][r] = 0.f;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) f.lacc[r] = 0.f;
+  // Q codes: bytes 16*hl .. +15 and 32 + 16*hl .. +15 of each 64-dim step
+  const bool valid = f.qi < N;
+  const int64_t qrow = (int64_t)bh * N + f.qi;
+#pragma unroll
+  for (int kk = 0; kk < F::KS; ++kk) {
+    u32x4 a0 = {0u, 0u, 0u, 0u}, a1 = {0u, 0u, 0u, 0u};
+    if (valid) {
+      const unsigned char* src = q8 + qrow * D + 64 * kk + 16 * f.hl;
+      a0 = *reinterpret_cast<const u32x4*>(src);
+      a1 = *reinterpret_cast<const u32x4*>(src + 32);
+    }
+    f.qf[kk] = __builtin_bit_cast(i32x8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
+  }
+  {
+    unsigned w = 0;
+    if (valid) {
+      if constexpr (D == 128) w = *reinterpret_cast<const unsigned*>(qs + qrow * 4);
+      else w = *reinterpret_cast<const unsigned short*>(qs + qrow * 2);
+    }
+    f.qsc = D == 128 ? (int)(((w >> (8 * f.hl)) & 0xFF) | (((w >> (16 + 8 * f.hl)) & 0xFF) << 8))
+                     : (int)((w >> (8 * f.hl)) & 0xFF);
+  }
+#pragma unroll
+  for (int i = 0; i < C::kDmaPerWave; ++i)
+    f.koff[i] = f8_dma_offset((f.wave + kF8Waves * i) * 64 + lane, C::kStride, D);
+#pragma unroll
+  for (int i = 0; i < C::vDmaPerWave; ++i)
+    f.voff[i] = f8_dma_offset((f.wave + kF8Waves * i) * 64 + lane, C::vStride, kF8Keys);
+  f.k_rd = f.l32 * C::kStride + 16 * f.hl;
+  f.v_rd = f.l32 * C::vStride + 32 * f.hl;
+
+  const int kv_end = CAUSAL ? min(N, q0 + BR) : N;
+  const int n_tiles = (kv_end + kF8Keys - 1) / kF8Keys;
+  const int n_full = CAUSAL ? min(q0 + 1, N) / kF8Keys : N / kF8Keys;
+
+  f.template issue<0>(0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  int j = 0;
+  const int full_end = min(n_tiles, n_full);
+  for (; j + 1 < full_end; j += 2) {
+    f.template step<false, 0>(j, n_tiles);
+    f.template step<false, 1>(j + 1, n_tiles);
+  }
+  if (j < full_end) {
+    f.template step<false, 0>(j, n_tiles);
+    ++j;
+  }
+  for (; j < n_tiles; ++j) {
+    if (j & 1) f.template step<true, 1>(j, n_tiles);
+    else       f.template step<true, 0>(j, n_tiles);
+  }
+
+  if (!valid) return;
+  const float l_tot = f.lacc[0];
+  const float inv = 1.f / l_tot;
+  unsigned short* orow = o + qrow * D;
+#pragma unroll
+  for (int db = 0; db < F::DB; ++db)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int dim = 32 * db + 8 * g + 4 * f.hl;
+      const u32x2 w = {pack_bf16x2(f.acc[db][4 * g] * inv, f.acc[db][4 * g + 1] * inv),
+                       pack_bf16x2(f.acc[db][4 * g + 2] * inv, f.acc[db][4 * g + 3] * inv)};
+      *reinterpret_cast<u32x2*>(orow + dim) = w;
+    }
+  if (f.hl == 0) lse[qrow] = f.m * scale + logf(l_tot);
+}
+
+template <int D>
+hipError_t launch_quant_rows(const void* x, int64_t rows, void* x8, void* xs, hipStream_t stream) {
+  const int64_t threads = rows * (D / 32);
+  hipLaunchKernelGGL((quant_rows_kernel<D>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream,
+                     static_cast<const unsigned short*>(x), rows, static_cast<unsigned char*>(x8),
+                     static_cast<unsigned char*>(xs));
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_quant_v(const void* v, int BH, int N, void* v8t, void* vs, hipStream_t stream) {
+  const int T = (N + kF8Keys - 1) / kF8Keys;
+  const int64_t threads = (int64_t)BH * T * 2 * D;
+  hipLaunchKernelGGL((quant_v_kernel<D>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream,
+                     static_cast<const unsigned short*>(v), BH, N, T, static_cast<unsigned char*>(v8t),
+                     static_cast<unsigned char*>(vs));
+  return hipGetLastError();
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch_fp8(const Fp8Problem& p, hipStream_t stream) {
+  const int BH = p.B * p.H;
+  const int n_qtiles = (p.N + 32 * kF8Waves - 1) / (32 * kF8Waves);
+  hipLaunchKernelGGL((fwd_fp8_kernel<D, CAUSAL>), dim3((unsigned)((int64_t)n_qtiles * BH)),
+                     dim3(kF8Threads), 0, stream, static_cast<const unsigned char*>(p.q8),
+                     static_cast<const unsigned char*>(p.qs), static_cast<const unsigned char*>(p.k8),
+                     static_cast<const unsigned char*>(p.ks), static_cast<const unsigned char*>(p.v8t),
+                     static_cast<const unsigned char*>(p.vs), static_cast<unsigned short*>(p.o), p.lse, p.N,
+                     BH, n_qtiles, p.scale);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_quantize_qk_fp8(const void* x, int64_t rows, int d, void* x8, void* xs, hipStream_t stream) {
+  return d == 64 ? launch_quant_rows<64>(x, rows, x8, xs, stream) : launch_quant_rows<128>(x, rows, x8, xs, stream);
+}
+
+hipError_t launch_quantize_v_fp8(const void* v, int BH, int N, int d, void* v8t, void* vs, hipStream_t stream) {
+  return d == 64 ? launch_quant_v<64>(v, BH, N, v8t, vs, stream) : launch_quant_v<128>(v, BH, N, v8t, vs, stream);
+}
+
+hipError_t launch_fwd_fp8(const Fp8Problem& p, hipStream_t stream) {
+  if (p.d == 64) return p.causal ? launch_fp8<64, true>(p, stream) : launch_fp8<64, false>(p, stream);
+  return p.causal ? launch_fp8<128, true>(p, stream) : launch_fp8<128, false>(p, stream);
+}
+
+}  // namespace fa

@@ -58,6 +58,27 @@ inline int64_t bwd_workspace_bytes(int B, int H, int N) {
   return ((int64_t)B * H * N * 4 + 255) / 256 * 256;
 }
 
+// fp8 problem (square): MX-quantized Q, K (codes [B*H*N, d], E8M0 scales
+// [B*H*N, d/32]) and V (transposed 64-key tiles and their scales, as written
+// by the V quantizer); o bf16 [B,H,N,d], lse fp32 [B,H,N].
+struct Fp8Problem {
+  const void* q8;
+  const void* qs;
+  const void* k8;
+  const void* ks;
+  const void* v8t;
+  const void* vs;
+  void* o;
+  float* lse;
+  int B, H, N, d;
+  float scale;
+  int causal;
+};
+
+// Bytes of the quantized V of B*H heads: codes and scales.
+inline int64_t fp8_v_code_bytes(int64_t BH, int N, int d) { return BH * ((N + 63) / 64) * d * 64; }
+inline int64_t fp8_v_scale_bytes(int64_t BH, int N, int d) { return BH * ((N + 63) / 64) * 2 * d; }
+
 // Query rows per workgroup tile of the bf16 kernel.
 constexpr int kTileRows = 128;
 
@@ -101,5 +122,8 @@ inline SplitLayout splitkv_layout(int B, int H, int Nq, int d, int splits) {
 hipError_t launch_fwd_f32(const Problem& p, hipStream_t stream);
 hipError_t launch_fwd_bf16(const GqaProblem& p, hipStream_t stream);
 hipError_t launch_bwd_bf16(const BwdProblem& p, hipStream_t stream);
+hipError_t launch_quantize_qk_fp8(const void* x, int64_t rows, int d, void* x8, void* xs, hipStream_t stream);
+hipError_t launch_quantize_v_fp8(const void* v, int BH, int N, int d, void* v8t, void* vs, hipStream_t stream);
+hipError_t launch_fwd_fp8(const Fp8Problem& p, hipStream_t stream);
 
 }  // namespace fa

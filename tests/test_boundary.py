@@ -215,3 +215,46 @@ def test_bwd_workspace_size():
     assert fa.fa_bwd_workspace_size(1, 1, 3, 128) == 256
     assert fa.fa_bwd_workspace_size(1, 1, 3, 80) == 0
     assert fa.fa_bwd_workspace_size(0, 1, 3, 64) == 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=None), fa.FA_ERR_NULL), (dict(xs=None), fa.FA_ERR_NULL), (dict(rows=0), fa.FA_ERR_SHAPE),
+    (dict(d=96), fa.FA_ERR_UNSUPPORTED_D), (dict(x8=A + 8 * MB + 4), fa.FA_ERR_ALIGN),
+    (dict(x8=A + 64), fa.FA_ERR_ALIAS), (dict(xs=A + 8 * MB + 128), fa.FA_ERR_ALIAS),
+])
+def test_quantize_qk_fp8_bad_arguments(kw, status):
+    a = dict(x=A, rows=64, d=64, x8=A + 8 * MB, xs=A + 16 * MB, stream=None)
+    a.update(kw)
+    assert fa.fa_quantize_qk_fp8(a["x"], a["rows"], a["d"], a["x8"], a["xs"], a["stream"]) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(v=None), fa.FA_ERR_NULL), (dict(vs=None), fa.FA_ERR_NULL), (dict(BH=0), fa.FA_ERR_SHAPE),
+    (dict(N=0), fa.FA_ERR_SHAPE), (dict(d=32), fa.FA_ERR_UNSUPPORTED_D),
+    (dict(vs=A + 16 * MB + 2), fa.FA_ERR_ALIGN), (dict(v8t=A + 32), fa.FA_ERR_ALIAS),
+])
+def test_quantize_v_fp8_bad_arguments(kw, status):
+    a = dict(v=A, BH=2, N=100, d=128, v8t=A + 8 * MB, vs=A + 16 * MB, stream=None)
+    a.update(kw)
+    assert fa.fa_quantize_v_fp8(a["v"], a["BH"], a["N"], a["d"], a["v8t"], a["vs"], a["stream"]) == status
+
+
+def test_fp8_v_sizes():
+    assert fa.fa_fp8_v_bytes(2, 100, 128) == 2 * 2 * 128 * 64
+    assert fa.fa_fp8_v_scale_bytes(2, 100, 128) == 2 * 2 * 2 * 128
+    assert fa.fa_fp8_v_bytes(1, 64, 64) == 64 * 64 and fa.fa_fp8_v_bytes(1, 64, 80) == 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q8=None), fa.FA_ERR_NULL), (dict(vs=None), fa.FA_ERR_NULL), (dict(lse=None), fa.FA_ERR_NULL),
+    (dict(N=0), fa.FA_ERR_SHAPE), (dict(d=256), fa.FA_ERR_UNSUPPORTED_D),
+    (dict(scale=-1.0), fa.FA_ERR_SCALE), (dict(causal=3), fa.FA_ERR_CAUSAL),
+    (dict(ks=A + 24 * MB + 1), fa.FA_ERR_ALIGN), (dict(o=A + 8 * MB), fa.FA_ERR_ALIAS),
+    (dict(lse=A + 40 * MB + 16), fa.FA_ERR_ALIAS), (dict(lse=A + 48 * MB), fa.FA_ERR_ALIAS),
+])
+def test_fwd_fp8_bad_arguments(kw, status):
+    a = dict(q8=A, qs=A + 8 * MB, k8=A + 16 * MB, ks=A + 24 * MB, v8t=A + 32 * MB, vs=A + 40 * MB,
+             o=A + 48 * MB, lse=A + 56 * MB, B=1, H=2, N=64, d=64, scale=0.125, causal=0, stream=None)
+    a.update(kw)
+    assert fa.fa_fwd_fp8(a["q8"], a["qs"], a["k8"], a["ks"], a["v8t"], a["vs"], a["o"], a["lse"], a["B"],
+                         a["H"], a["N"], a["d"], a["scale"], a["causal"], a["stream"]) == status

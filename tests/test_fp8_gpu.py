@@ -1,0 +1,219 @@
+"""Parity of the fp8 path: the MX block quantizers bit for bit against the
+oracle's quantization, and the fp8 attention forward against the oracle's
+attention of the dequantized inputs.
+
+Tolerance of the attention (derived from the arithmetic, per element):
+the kernel rounds the probabilities P to E4M3 before the product with V and
+sums the same rounded values for the denominator.  Rounding P_j changes
+weight w_j = P_j / l by at most max(delta * w_j, 2^-10 / l) with
+delta = 2^-4 (half an E4M3 step, relative, for normal values; 2^-10 absolute
+below 2^-6, in units where the row's largest P is at least 1, so l >= 1).
+These errors are independent across keys, so the error of O_c is a sum of
+independent terms with standard deviation
+    sigma_c = sqrt(sum_j e_j^2 / 3 * (v_jc - O_c)^2),  e_j = max(delta w_j, 2^-10 / l)
+and the test allows 8 sigma_c, plus half a bf16 step of O (2^-9 |O|, doubled)
+and 3e-4 max_j |v_jc| for the fp8 matrix cores' internal accumulation
+(measured at about 1e-4 of the largest partial sum).  LSE gets
+8 sqrt(sum_j e_j^2 / 3) + 1e-3.  Inputs whose probabilities are all powers of
+two (exact in E4M3) leave only the last two terms: there the bound is
+4e-3 max|O| for O and 1e-3 for LSE.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import mx_fp8 as mx
+from io_aware_softmax_fwd_amd import workloads as W
+
+from gpu_util import note, torch_or_skip, upload
+
+pytestmark = pytest.mark.gpu
+
+DELTA = 2.0 ** -4
+
+
+def _bf(shape, seed, scale=1.0):
+    x = np.random.default_rng(seed).standard_normal(shape, dtype=np.float32) * scale
+    return W.bf16_bits_to_f32(W.bf16_bits_rne(x))
+
+
+def _perm():
+    """Key (inside a 64-key tile) held by position p = 32h + j of a tile row."""
+    return np.array([32 * (j // 16) + (j % 4) + 8 * ((j % 16) // 4) + 4 * h
+                     for h in (0, 1) for j in range(32)])
+
+
+def _v_logical(v8t, vs, BH, N, d):
+    """GPU V layout -> codes [BH, T*64, d] and scales [BH, 2T, d] in key order."""
+    T = (N + 63) // 64
+    tiles = v8t.reshape(BH, T, d, 64).transpose(0, 1, 3, 2)        # [BH, T, position, d]
+    codes = np.zeros((BH, T, 64, d), dtype=np.uint8)
+    codes[:, :, _perm(), :] = tiles
+    scales = vs.reshape(BH, T, 2, 32, d // 32).transpose(0, 1, 2, 4, 3).reshape(BH, 2 * T, d)
+    return codes.reshape(BH, T * 64, d), scales
+
+
+def _oracle_quant(q, k, v):
+    """Oracle MX quantization of q, k, v ([B,H,N,d] float32): codes, scales and
+    the dequantized float32 inputs (V padded to whole 64-key tiles)."""
+    B, H, N, d = q.shape
+    T = (N + 63) // 64
+    qc, qs = mx.mx_quantize(q, axis=-1)
+    kc, ks = mx.mx_quantize(k, axis=-1)
+    vp = np.zeros((B * H, T * 64, d), dtype=np.float32)
+    vp[:, :N] = v.reshape(B * H, N, d)
+    vc, vsc = mx.mx_quantize(vp, axis=-2)
+    deq = (mx.mx_dequantize(qc, qs), mx.mx_dequantize(kc, ks),
+           mx.mx_dequantize(vc, vsc, axis=-2)[:, :N].reshape(B, H, N, d))
+    return (qc, qs, kc, ks, vc, vsc), deq
+
+
+def _gpu_quant(q, k, v):
+    torch = torch_or_skip()
+    import io_aware_softmax_fwd_amd as fa
+    qd, kd, vd = upload(q, "bf16"), upload(k, "bf16"), upload(v, "bf16")
+    q8, qs = fa.quantize_qk_fp8(qd)
+    k8, ks = fa.quantize_qk_fp8(kd)
+    v8t, vs = fa.quantize_v_fp8(vd)
+    torch.cuda.synchronize()
+    return q8, qs, k8, ks, v8t, vs
+
+
+def _special_values(shape, seed):
+    """bf16 values spanning the scale rule's corner cases: block maxima just
+    at and above 1.75 * 2^k, zero blocks, bf16 subnormals, huge and tiny
+    rows, negative zeros."""
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal(shape).astype(np.float32)
+    x *= (2.0 ** rng.integers(-40, 40, size=shape[:-1] + (1,))).astype(np.float32)
+    flat = x.reshape(-1, shape[-1])
+    n = flat.shape[0]
+    flat[0::7, :32] = 0.0
+    flat[1::7, :32] = np.float32(1.75) * np.sign(flat[1::7, :32] + 0.5)
+    flat[2::7, 5] = np.float32(1.7578125) * 8             # first bf16 above 1.75, scaled
+    flat[3::7, :] *= np.float32(1e-38)                    # float32/bf16 subnormals
+    flat[4::7, 3] = -0.0
+    flat[5::7, :] = np.float32(448.0)
+    x = flat.reshape(shape)
+    return W.bf16_bits_to_f32(W.bf16_bits_rne(x))
+
+
+@pytest.mark.parametrize("N,d", [(100, 64), (300, 128), (64, 128), (1, 64)])
+def test_quantizers_bit_exact(N, d):
+    torch_or_skip()
+    B, H = 1, 3
+    note("fp8 quantizers N=%d d=%d" % (N, d))
+    q = _special_values((B, H, N, d), 1 + N)
+    k = _bf((B, H, N, d), 2 + N, 3.0)
+    v = _special_values((B, H, N, d), 3 + N)
+    g = [t.cpu().numpy() for t in _gpu_quant(q, k, v)]
+    (qc, qs, kc, ks, vc, vsc), _ = _oracle_quant(q, k, v)
+    assert np.array_equal(g[0], qc) and np.array_equal(g[1], qs)
+    assert np.array_equal(g[2], kc) and np.array_equal(g[3], ks)
+    gvc, gvs = _v_logical(g[4], g[5], B * H, N, d)
+    assert np.array_equal(gvs, vsc)
+    assert np.array_equal(gvc, vc)
+
+
+def _bounds(qd, kd, vd, scale, causal, rows, O_ref):
+    """Per-element O bound and per-row LSE bound of the docstring for the
+    listed flat rows (float64 numpy on the dequantized inputs)."""
+    B, H, N, d = qd.shape
+    ob = np.empty((len(rows), d))
+    lb = np.empty(len(rows))
+    for t, r in enumerate(rows):
+        bh, i = divmod(int(r), N)
+        b, h = divmod(bh, H)
+        nk = i + 1 if causal else N
+        s = scale * (kd[b, h, :nk].astype(np.float64) @ qd[b, h, i].astype(np.float64))
+        p = np.exp(s - s.max())
+        l = p.sum()
+        w = p / l
+        e = np.maximum(DELTA * w, 2.0 ** -10 / l)
+        vv = vd[b, h, :nk].astype(np.float64)
+        sig = np.sqrt((e[:, None] ** 2 / 3 * (vv - O_ref[t][None, :]) ** 2).sum(axis=0))
+        ob[t] = 8 * sig + 2.0 ** -8 * np.abs(O_ref[t]) + 3e-4 * np.abs(vv).max(axis=0)
+        lb[t] = 8 * math.sqrt((e ** 2).sum() / 3) + 1e-3
+    return ob, lb
+
+
+def _run_fp8(q8, qs, k8, ks, v8t, vs, scale, causal):
+    torch = torch_or_skip()
+    import io_aware_softmax_fwd_amd as fa
+    o, lse = fa.fwd_fp8(q8, qs, k8, ks, v8t, vs, scale=scale, causal=causal)
+    torch.cuda.synchronize()
+    return o.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
+
+
+def _check_rows(O, L, deq, scale, causal, rows, what):
+    qd, kd, vd = deq
+    B, H, N, d = qd.shape
+    O_ref, L_ref = oracle.attention_c(qd, kd, vd, scale, causal, rows=rows)
+    Og = O.reshape(-1, d)[rows]
+    Lg = L.reshape(-1)[rows]
+    assert np.all(np.isfinite(Og)) and np.all(np.isfinite(Lg)), what + ": non-finite"
+    ob, lb = _bounds(qd, kd, vd, scale, causal, rows, O_ref)
+    eo = np.abs(Og - O_ref)
+    el = np.abs(Lg - L_ref)
+    note("%s: max|dO|=%.3e (max|O| %.3e), worst dO/bound=%.3f, max|dLSE|=%.3e, worst dLSE/bound=%.3f"
+         % (what, eo.max(), np.abs(O_ref).max(), (eo / ob).max(), el.max(), (el / lb).max()))
+    assert np.all(eo <= ob), what + ": O outside the derived bound"
+    assert np.all(el <= lb), what + ": LSE outside the derived bound"
+
+
+@pytest.mark.parametrize("B,H,N,d,causal", [(1, 2, 300, 64, True), (2, 2, 257, 128, False),
+                                             (1, 1, 1000, 128, True), (1, 2, 64, 64, False),
+                                             (1, 1, 1, 128, True)])
+def test_fp8_random_within_derived_bound(B, H, N, d, causal):
+    torch_or_skip()
+    case = "fp8 random B=%d H=%d N=%d d=%d causal=%d" % (B, H, N, d, causal)
+    note(case)
+    q, k, v = (_bf((B, H, N, d), 40 + N + d + t) for t in range(3))
+    scale = float(np.float32(1 / math.sqrt(d)))
+    O, L = _run_fp8(*_gpu_quant(q, k, v), scale, causal)
+    _, deq = _oracle_quant(q, k, v)
+    _check_rows(O, L, deq, scale, causal, np.arange(B * H * N), case)
+
+
+@pytest.mark.parametrize("N,d,causal", [(300, 64, True), (257, 128, False), (700, 128, True)])
+def test_fp8_exact_probabilities_tight(N, d, causal):
+    """Scores are small integers and scale = ln 2, so every probability the
+    kernel forms is a power of two between 2^-9 and 2^8: exact in E4M3."""
+    torch_or_skip()
+    case = "fp8 exact-P N=%d d=%d causal=%d" % (N, d, causal)
+    note(case)
+    rng = np.random.default_rng(N + d)
+    B, H = 1, 2
+    q = np.zeros((B, H, N, d), dtype=np.float32)
+    k = np.zeros((B, H, N, d), dtype=np.float32)
+    idx = np.arange(N)
+    for h in range(H):
+        q[0, h, idx, rng.integers(0, 4, N)] = rng.integers(0, 4, N)
+        k[0, h, idx, rng.integers(0, 4, N)] = rng.integers(0, 4, N)
+    v = _bf((B, H, N, d), 7 + N)
+    scale = float(np.float32(math.log(2.0)))
+    O, L = _run_fp8(*_gpu_quant(q, k, v), scale, causal)
+    _, deq = _oracle_quant(q, k, v)
+    assert np.array_equal(deq[0], q) and np.array_equal(deq[1], k)   # integers survive exactly
+    O_ref, L_ref = oracle.attention_c(*deq, scale, causal)
+    eo, el = np.abs(O - O_ref).max(), np.abs(L - L_ref).max()
+    note("%s: max|dO|=%.3e (bound %.3e)  max|dLSE|=%.3e (bound 1e-3)" % (case, eo, 4e-3 * np.abs(O_ref).max(), el))
+    assert eo <= 4e-3 * np.abs(O_ref).max() and el <= 1e-3
+
+
+@pytest.mark.parametrize("cfg", [2, 3, 4, 5])
+def test_fp8_workload_shapes(cfg):
+    """The forward workloads' shapes and input recipes (C4 with its
+    amplified rows) on sampled rows, against the derived bound."""
+    torch_or_skip()
+    w = W.WORKLOADS[cfg]
+    if w.dtype != "bf16":
+        pytest.skip("bf16 workloads only")
+    note("fp8 workload C%d: %s" % (cfg, w.describe()))
+    x = W.make_inputs(w)
+    O, L = _run_fp8(*_gpu_quant(x["q"], x["k"], x["v"]), w.scale, w.causal)
+    _, deq = _oracle_quant(x["q"], x["k"], x["v"])
+    rows = W.sample_rows(w, 256, seed=cfg + 50)
+    _check_rows(O, L, deq, w.scale, w.causal, rows, "C%d" % cfg)
