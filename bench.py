@@ -149,10 +149,19 @@ PROFILE_STEPS = {
                   "-- python bench.py --decode 131072 --hkv 8",
     "decode_mha": "rocprofv3 --kernel-trace --stats --output-format csv -d $OUT/decode_mha -o run "
                   "-- python bench.py --decode 131072",
+    "bwd": "rocprofv3 --kernel-trace --stats --output-format csv -d $OUT/bwd -o run "
+           "-- python bench.py --bwd",
+    "fp8": "rocprofv3 --kernel-trace --stats --output-format csv -d $OUT/fp8 -o run "
+           "-- python bench.py --fp8",
+    "gqa": "rocprofv3 --kernel-trace --stats --output-format csv -d $OUT/gqa -o run "
+           "-- python bench.py --hkv 8 --no-cpu-baseline",
 }
 # extra kernel-trace steps summarised kernel by kernel: step -> summary name
-TRACE_ONLY = {"decode_gqa": "decode_b1_h32_hkv8_nk131072_d128",
-              "decode_mha": "decode_b1_h32_nk131072_d128"}
+TRACE_ONLY = {"decode_gqa": "fa_fwd_gqa_decode_b1_h32_hkv8_nk131072_d128",
+              "decode_mha": "fa_fwd_splitkv_decode_b1_h32_nk131072_d128",
+              "bwd": "fa_bwd_bf16_n16k_d128_causal_amplified",
+              "fp8": "fa_fwd_fp8_bf16_n16k_d128_causal_amplified",
+              "gqa": "fa_fwd_gqa_hkv8_bf16_n16k_d128_causal_amplified"}
 KERNEL_KEY = "fwd_bf16_kernel"
 COPY_KEY = "copy"
 
@@ -238,11 +247,11 @@ def summarize(out_dir, workload_name):
         out = []
         with open(st[0]) as fh:
             for row in csv.DictReader(fh):
-                if "fa" in row["Name"] and ("fwd_bf16_kernel" in row["Name"] or "merge" in row["Name"]):
+                if "fa::" in row["Name"]:
                     out.append("kernel: %s\ncalls=%s  average=%.2f us  min=%.2f us  max=%.2f us" % (
                         row["Name"], row["Calls"], float(row["AverageNs"]) / 1e3,
                         float(row["MinNs"]) / 1e3, float(row["MaxNs"]) / 1e3))
-        with open(os.path.join(prof, "fa_fwd_bf16_%s_kernel_trace.txt" % name), "w") as f:
+        with open(os.path.join(prof, "%s_kernel_trace.txt" % name), "w") as f:
             f.write("# rocprofv3 kernel trace, %s (kernel source %s)\n" % (name, src_hash))
             f.write("# command: %s\n" % PROFILE_STEPS[step])
             f.write("\n".join(out) + "\n")
