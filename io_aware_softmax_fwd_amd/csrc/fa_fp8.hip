@@ -287,12 +287,13 @@ struct FwdF8 {
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
-        int word = 0;
         const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kb][4 * w], c, -mc));
         const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kb][4 * w + 1], c, -mc));
         const float p2 = __builtin_amdgcn_exp2f(fmaf(s[kb][4 * w + 2], c, -mc));
         const float p3 = __builtin_amdgcn_exp2f(fmaf(s[kb][4 * w + 3], c, -mc));
-        word = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, word, false);
+        // bytes 0-1 first (bytes 2-3 of the old value are overwritten next,
+        // so any register serves as the old value), then bytes 2-3
+        int word = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, __builtin_bit_cast(int, p0), false);
         word = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, word, true);
         pf[4 * kb + w] = word;
       }

@@ -29,11 +29,14 @@
 // the buffers being read, so the loads get the whole step to land.
 // LDS rows are padded so that fragment reads hit distinct banks with every
 // lane's addresses a compile-time offset from one base.
-// Rescaling is lazy: the running max used as the exponent's offset only moves
-// when a row's max exceeds it by more than 8/c (c = scale*log2 e), so
-// probabilities stay <= 2^8 and the accumulator is rescaled rarely; since O
-// and l share the offset the result is unchanged (the softmax identity holds
-// for any offset; zzszmyf.github.io notes, section 5.1).
+// Rescaling is lazy and needs no row max on most tiles: a tile's
+// probabilities are first taken against the current offset m; they are kept
+// when no lane's share of their sum exceeds 2^32 (so no probability does
+// either).  Only otherwise (a row's first tile, where m = -inf, or a score far
+// above m) is the row max taken, m moved to it, the accumulator rescaled by
+// exp(m_old - m_new) and the probabilities redone.  Since O and l share the
+// offset the result is unchanged (the softmax identity holds for any offset;
+// zzszmyf.github.io notes, section 5.1).
 // Causal: key tiles wholly above the diagonal are never loaded, masking is
 // applied only on diagonal tiles and on the ragged last tile.
 // Grouped K/V heads (MQA/GQA, the K/V-read saving named in the aiqz.cc
@@ -54,7 +57,10 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kKeys = 64;                 // keys per K/V tile (Bc)
-constexpr float kLazy = 8.0f;             // log2 headroom before a rescale
+// A tile's probabilities against a stale offset are kept while every lane's
+// share of their sum (32 of them) is at most this, so a row sum grows by at
+// most 2^27 per key: far from the fp32 range limit.
+constexpr float kProbSumMax = 4294967296.0f;
 
 template <int D> struct Cfg {
   // K rows carry one 16-byte pad chunk, so the 16-byte fragment reads of 16
@@ -86,7 +92,7 @@ struct Fwd {
   int wave, l32, hl;
   int pos[QB];            // position inside its head of this lane's query, per block
   int wlast;              // causal: last key any valid query of this wave sees (-1: none)
-  float c, thr;
+  float c;                // scale * log2(e)
   bf16x8 qf[QB][KS];      // Q fragments (B operand of S^T = K Q^T), per 32-row block
   f32x16 acc[QB][DB];     // O^T accumulators: lane holds query l%32 of each block
   float m[QB];            // exponent offsets (raw-score units)
@@ -133,48 +139,13 @@ struct Fwd {
 #endif
   }
 
-  // Online-softmax step of one 32-row block for the tile at key k0: moves
-  // the offset when needed (rescaling its accumulator), writes the bf16
-  // probabilities and adds their row sum.
-  template <bool MASK>
-  __device__ void softmax(int qb, f32x16 (&s)[KB], bf16x8 (&pf)[PS], int k0) {
-    if constexpr (MASK) {
-      // key = k0 + 32*kb + (r&3) + 8*(r>>2) + 4*hl must be <= min(qi+coff, N-1)
-      const int lim = (CAUSAL ? min(pos[qb] + coff, N - 1) : N - 1) - k0 - 4 * hl;
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (32 * kb + (r & 3) + 8 * (r >> 2) > lim) s[kb][r] = -INFINITY;
-    }
-    float mx = s[0][0];
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-      for (int r = (kb == 0 ? 1 : 0); r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-    mx = max_across_halves(mx);
-    // Move the offset only when this row's max ran more than `thr` past it
-    // (always on the first tile, where m = -inf).
-    const bool upd = mx > m[qb] + thr;
-    if (__builtin_amdgcn_ballot_w64(upd)) {
-      asm volatile("" ::: "memory");   // keep this a taken/skipped branch
-      const float m_new = upd ? mx : m[qb];
-      // 0 at the start (m = -inf); exactly 1 for rows that keep their offset
-      // (also when that offset is still -inf, which the key-split path meets)
-      const float alpha = upd ? __builtin_amdgcn_exp2f((m[qb] - m_new) * c) : 1.f;
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[qb][db][r] *= alpha;
-      l[qb] *= alpha;
-      m[qb] = m_new;
-    }
-    // A split chunk can hold no valid key for a row (m still -inf): its
-    // probabilities must come out 0, not exp2(-inf + inf).
-    const float mc = (SPLIT && m[qb] == -INFINITY) ? 0.f : m[qb] * c;
-    // Probabilities, rounded to bf16 for the product; the row sum is taken
-    // over the same rounded values (two per v_dot2_f32_bf16), so numerator
-    // and denominator see identical weights.
+  // Probabilities of one 32-row block against the offset mc = m*c, rounded
+  // to bf16 for the product, and this lane's share of their sum, taken over
+  // the same rounded values (two per v_dot2_f32_bf16) so numerator and
+  // denominator see identical weights.  The dot2 takes the converted pair
+  // itself: taking it from an element of the vector under construction is
+  // miscompiled (the same element is summed repeatedly).
+  __device__ __forceinline__ float probs(const f32x16 (&s)[KB], bf16x8 (&pf)[PS], float mc) {
     float ps0 = 0.f, ps1 = 0.f;
     const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
@@ -186,9 +157,6 @@ struct Fwd {
         for (int e = 0; e < 8; e += 2) {
           const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * half + e], c, -mc));
           const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * half + e + 1], c, -mc));
-          // dot2 of the converted pair itself: taking it from an element of
-          // the vector under construction is miscompiled (the same element
-          // is summed repeatedly).
           const bf16x2 pb = __builtin_convertvector((f32x2{p0, p1}), bf16x2);
           if (e & 2) ps1 = __builtin_amdgcn_fdot2_f32_bf16(pb, ones, ps1, false);
           else       ps0 = __builtin_amdgcn_fdot2_f32_bf16(pb, ones, ps0, false);
@@ -196,7 +164,52 @@ struct Fwd {
         }
         pf[2 * kb + half] = __builtin_bit_cast(bf16x8, w);
       }
-    l[qb] += ps0 + ps1;
+    return ps0 + ps1;
+  }
+
+  // Online-softmax step of one 32-row block for the tile at key k0: writes
+  // the bf16 probabilities, moving the offset (and rescaling) when needed,
+  // and adds their row sum.
+  template <bool MASK>
+  __device__ void softmax(int qb, f32x16 (&s)[KB], bf16x8 (&pf)[PS], int k0) {
+    if constexpr (MASK) {
+      // key = k0 + 32*kb + (r&3) + 8*(r>>2) + 4*hl must be <= min(qi+coff, N-1)
+      const int lim = (CAUSAL ? min(pos[qb] + coff, N - 1) : N - 1) - k0 - 4 * hl;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (32 * kb + (r & 3) + 8 * (r >> 2) > lim) s[kb][r] = -INFINITY;
+    }
+    // Probabilities against the current offset, kept unless some lane's
+    // share of their sum is above kProbSumMax or NaN (m = -inf on a row's
+    // first tile gives inf or NaN); then the offset moves to the row max
+    // (wave-uniform branch; rows whose max did not rise keep alpha = 1) and
+    // they are redone.
+    float ps = probs(s, pf, m[qb] * c);
+    if (__builtin_amdgcn_ballot_w64(!(ps <= kProbSumMax))) {
+      asm volatile("" ::: "memory");
+      float mx = s[0][0];
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int r = (kb == 0 ? 1 : 0); r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+      mx = max_across_halves(mx);
+      const bool upd = mx > m[qb];
+      const float m_new = upd ? mx : m[qb];
+      const float alpha = upd ? __builtin_amdgcn_exp2f((m[qb] - m_new) * c) : 1.f;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[qb][db][r] *= alpha;
+      l[qb] *= alpha;
+      m[qb] = m_new;
+      // a key-split chunk can hold no valid key for a row (m still -inf):
+      // its probabilities must come out 0, not exp2(-inf + inf)
+      const float mc = (SPLIT && m_new == -INFINITY) ? 0.f : m_new * c;
+      ps = probs(s, pf, mc);
+    }
+    l[qb] += ps;
   }
 
   // Consume the tile in buffers PAR: S^T = K Q^T for every block (each K
@@ -339,7 +352,6 @@ __global__ __launch_bounds__(kThreads, QB == 1 ? 2 : 1) void fwd_bf16_kernel(
     }
   }
   f.c = scale * kLog2e;
-  f.thr = kLazy / f.c;
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     f.m[qb] = -INFINITY;
