@@ -27,8 +27,12 @@
 // compile time (the tile loop is unrolled by two); one barrier per tile.
 // Separate arrays let the compiler see that the in-flight loads never touch
 // the buffers being read, so the loads get the whole step to land.
-// LDS rows are padded so that fragment reads hit distinct banks with every
-// lane's addresses a compile-time offset from one base.
+// LDS rows are unpadded (2*D bytes, so every LDS-DMA byte is data): the
+// 16-byte chunks of each row are permuted by an XOR swizzle of the row, set
+// when the DMA source offsets are chosen, so that the K fragment reads of 16
+// rows and the transposed V reads of 4 rows fall in distinct banks.  A
+// lane's read addresses are then one register per K k-step and per V
+// head-dim block, plus compile-time offsets.
 // Rescaling is lazy and needs no row max on most tiles: a tile's
 // probabilities are first taken against the current offset m; they are kept
 // when no lane's share of their sum exceeds 2^32 (so no probability does
@@ -63,12 +67,10 @@ constexpr int kKeys = 64;                 // keys per K/V tile (Bc)
 constexpr float kProbSumMax = 4294967296.0f;
 
 template <int D> struct Cfg {
-  // K rows carry one 16-byte pad chunk, so the 16-byte fragment reads of 16
-  // consecutive rows fall in distinct bank groups.  V rows are padded so that
-  // the four rows a transposed read touches land in four distinct quarters
-  // of the banks.
-  static constexpr int kStride = 2 * D + 16;           // bytes per K row
-  static constexpr int vStride = D == 128 ? 320 : 192; // bytes per V row
+  // Rows are stored unpadded (2*D bytes); each row's 16-byte chunks are
+  // permuted by an XOR swizzle so that fragment reads stay conflict-free.
+  static constexpr int kStride = 2 * D;                // bytes per K row
+  static constexpr int vStride = 2 * D;                // bytes per V row
   static constexpr int kTile = kKeys * kStride;        // bytes of one K tile
   static constexpr int vTile = kKeys * vStride;        // bytes of one V tile
   static constexpr int lds = 2 * (kTile + vTile);      // two K and two V buffers
@@ -76,6 +78,10 @@ template <int D> struct Cfg {
   static constexpr int vDma = vTile / 1024;
   static constexpr int kDmaPerWave = (kDma + kWaves - 1) / kWaves;
   static constexpr int vDmaPerWave = (vDma + kWaves - 1) / kWaves;
+  static constexpr int CH = D / 8;                     // 16-byte chunks per row
+  // physical chunk = logical chunk ^ swizzle(row)
+  static __device__ __forceinline__ int kswz(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
+  static __device__ __forceinline__ int vswz(int r) { return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
 };
 
 // SPLIT: the workgroup covers one chunk of the keys and may meet rows that
@@ -99,7 +105,8 @@ struct Fwd {
   float l[QB];            // this lane's share of the row sums, relative to m
   int koff[Cfg<D>::kDmaPerWave];   // source byte offsets of the K LDS-DMA slots
   int voff[Cfg<D>::vDmaPerWave];   // source byte offsets of the V LDS-DMA slots
-  int k_rd, v_rd;                  // this lane's fragment read offsets in a buffer
+  int k_rd[KS];                    // this lane's K fragment read offset for each k-step
+  int v_rd[DB];                    // this lane's V fragment read offset for each head-dim block
   // LDS: K and V of two tiles, as four separate arrays selected at compile
   // time, so the compiler sees that the LDS-DMA writes into one buffer do not
   // touch the buffers being read and inserts no wait for them.
@@ -107,17 +114,33 @@ struct Fwd {
   unsigned char* vbuf[2];
 
   __device__ void setup_offsets(int lane) {
+    // LDS-DMA slot (16 bytes) -> source: row = slot / CH, physical chunk =
+    // slot % CH holds logical chunk physical ^ swizzle(row)
 #pragma unroll
-    for (int i = 0; i < Cfg<D>::kDmaPerWave; ++i)
-      koff[i] = dma_offset<D>((wave + kWaves * i) * 64 + lane, Cfg<D>::kStride);
+    for (int i = 0; i < Cfg<D>::kDmaPerWave; ++i) {
+      const int slot = (wave + kWaves * i) * 64 + lane;
+      const int r = slot / Cfg<D>::CH, pc = slot % Cfg<D>::CH;
+      koff[i] = r * (2 * D) + 16 * (pc ^ Cfg<D>::kswz(r));
+    }
 #pragma unroll
-    for (int i = 0; i < Cfg<D>::vDmaPerWave; ++i)
-      voff[i] = dma_offset<D>((wave + kWaves * i) * 64 + lane, Cfg<D>::vStride);
-    k_rd = l32 * Cfg<D>::kStride + 16 * hl;
+    for (int i = 0; i < Cfg<D>::vDmaPerWave; ++i) {
+      const int slot = (wave + kWaves * i) * 64 + lane;
+      const int r = slot / Cfg<D>::CH, pc = slot % Cfg<D>::CH;
+      voff[i] = r * (2 * D) + 16 * (pc ^ Cfg<D>::vswz(r));
+    }
+    // K fragment of k-step ks: row l32 (+32 kb), logical chunk 2 ks + hl
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      k_rd[ks] = l32 * Cfg<D>::kStride + 16 * ((2 * ks + hl) ^ Cfg<D>::kswz(l32));
     // Transposed V reads: in each 16-lane group g, lane 4e + j addresses key
-    // row 4*(g/2) + e and head dims 16*(g%2) + 4j .. +3 of a 32-dim block.
+    // row 4*(g/2) + e (+8, +16 ps: the swizzle is unchanged) and head dims
+    // 16*(g%2) + 4j .. +3 of 32-dim block db, i.e. logical chunk
+    // 4 db + 2 (g%2) + j/2, byte 8 (j%2) within it.
     const int g = lane >> 4, e = (lane >> 2) & 3, j = lane & 3;
-    v_rd = (4 * (g >> 1) + e) * Cfg<D>::vStride + 2 * (16 * (g & 1) + 4 * j);
+    const int vr = 4 * (g >> 1) + e;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+      v_rd[db] = vr * Cfg<D>::vStride + 16 * ((4 * db + 2 * (g & 1) + (j >> 1)) ^ Cfg<D>::vswz(vr)) + 8 * (j & 1);
   }
 
   // Queue this wave's share of K (or V) of the tile at key k0 into LDS
@@ -217,8 +240,8 @@ struct Fwd {
   // (each V fragment feeds all blocks).
   template <bool MASK, int PAR>
   __device__ void consume(int k0) {
-    const unsigned char* kt = kbuf[PAR] + k_rd;
-    const unsigned char* vt = vbuf[PAR] + v_rd;
+    const unsigned char* kt = kbuf[PAR];
+    const unsigned char* vt = vbuf[PAR];
     f32x16 s[QB][KB];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb)
@@ -230,7 +253,7 @@ struct Fwd {
     for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kt + 32 * kb * Cfg<D>::kStride + 32 * ks);
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kt + k_rd[ks] + 32 * kb * Cfg<D>::kStride);
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
           s[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[qb][ks], s[qb][kb], 0, 0, 0);
@@ -244,7 +267,7 @@ struct Fwd {
     for (int ps = 0; ps < PS; ++ps)
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        const unsigned char* src = vt + 16 * ps * Cfg<D>::vStride + 64 * db;
+        const unsigned char* src = vt + v_rd[db] + 16 * ps * Cfg<D>::vStride;
         const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)src);
         const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(src + 8 * Cfg<D>::vStride));
         const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
