@@ -22,7 +22,8 @@
 // round-to-nearest-even E4M3 values of x * 2^(127 - E).
 //
 // The attention kernel follows the bf16 one (transposed products, online
-// softmax with a lazy offset, K/V tiles streamed by LDS-DMA, two buffers):
+// softmax with a lazy offset, K/V tiles streamed by LDS-DMA into two
+// buffers of unpadded, XOR-swizzled rows):
 //   S^T = K Q^T      v_mfma_scale 32x32x64, K codes from LDS (A), Q codes in
 //                    registers (B), their block scales applied by the MFMA;
 //   P = exp2(...)    fp32, rounded to E4M3 (values <= 2^8 by the lazy
@@ -146,23 +147,30 @@ __global__ __launch_bounds__(256) void quant_v_kernel(const unsigned short* __re
 
 // ---------------------------------------------------------- attention
 template <int D> struct F8Cfg {
-  static constexpr int kStride = D + 16;               // bytes per K code row in LDS
-  static constexpr int vStride = 80;                   // bytes per V^T code row (64 + 16)
-  static constexpr int kTile = kF8Keys * kStride;      // 9 KB (d=128) or 5 KB (d=64)
-  static constexpr int vTile = D * vStride;            // 10 KB or 5 KB
+  // Unpadded LDS rows (every LDS-DMA byte is data); the 16-byte chunks of a
+  // row are permuted by an XOR swizzle of the row so that the fragment reads
+  // of 16 rows fall in distinct banks: K rows are D bytes (D/16 chunks),
+  // V^T rows 64 bytes (4 chunks).
+  static constexpr int kStride = D;                    // bytes per K code row in LDS
+  static constexpr int vStride = kF8Keys;              // bytes per V^T code row
+  static constexpr int kTile = kF8Keys * kStride;      // 8 KB (d=128) or 4 KB (d=64)
+  static constexpr int vTile = D * vStride;            // 8 KB or 4 KB
   static constexpr int kDma = kTile / 1024, vDma = vTile / 1024;
   static constexpr int kDmaPerWave = (kDma + kF8Waves - 1) / kF8Waves;
   static constexpr int vDmaPerWave = (vDma + kF8Waves - 1) / kF8Waves;
+  static constexpr int KCH = D / 16, VCH = kF8Keys / 16;   // chunks per row
   static_assert(kTile % 1024 == 0 && vTile % 1024 == 0, "tiles must be whole 1 KB blocks");
+  // physical chunk = logical chunk ^ swizzle(row)
+  static __device__ __forceinline__ int kswz(int r) { return D == 128 ? ((r >> 1) & 7) : ((r >> 2) & 3); }
+  static __device__ __forceinline__ int vswz(int r) { return (r >> 2) & 3; }
 };
 
-// Source offset (inside one tile) of LDS-DMA slot `slot` for LDS rows of
-// `stride` bytes holding `row_bytes` of data; pad slots re-fetch the last chunk.
-__device__ __forceinline__ int f8_dma_offset(int slot, int stride, int row_bytes) {
-  const int slots = stride / 16;
-  const int r = slot / slots;
-  const int cc = min(slot % slots, row_bytes / 16 - 1);
-  return r * row_bytes + 16 * cc;
+// Source offset (inside one tile) of LDS-DMA slot `slot` of a tile whose
+// rows hold `chunks` 16-byte chunks, swizzled by `swz`.
+template <typename SWZ>
+__device__ __forceinline__ int f8_dma_offset(int slot, int chunks, SWZ swz) {
+  const int r = slot / chunks, pc = slot % chunks;
+  return r * 16 * chunks + 16 * (pc ^ swz(r));
 }
 
 template <int D, bool CAUSAL>
@@ -183,7 +191,8 @@ struct FwdF8 {
   f32x16 lacc;                 // row sums (every element holds the lane's l)
   float m;
   int koff[C::kDmaPerWave], voff[C::vDmaPerWave];
-  int k_rd, v_rd;
+  int k_rd[2 * KS];             // K read offset of chunk 4 ks + 2 h + hl, index 2 ks + h
+  int v_rd[2];                 // V^T read offset of chunk 2 hl + h, index h
   unsigned ksw[2][2];          // K scale words of the key rows 32kb + l32, per buffer
   unsigned vsw[2];             // V scale word (byte db) per buffer
   unsigned char* kbuf[2];
@@ -228,8 +237,8 @@ struct FwdF8 {
 
   template <bool MASK, int PAR>
   __device__ void consume(int k0) {
-    const unsigned char* kt = kbuf[PAR] + k_rd;
-    const unsigned char* vt = vbuf[PAR] + v_rd;
+    const unsigned char* kt = kbuf[PAR];
+    const unsigned char* vt = vbuf[PAR];
     f32x16 s[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -241,9 +250,9 @@ struct FwdF8 {
                                     : ((w >> (8 * hl)) & 0xFF);
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const unsigned char* src = kt + 32 * kb * C::kStride + 64 * ks;
-        const u32x4 a0 = *reinterpret_cast<const u32x4*>(src);
-        const u32x4 a1 = *reinterpret_cast<const u32x4*>(src + 32);
+        const unsigned char* src = kt + 32 * kb * C::kStride;
+        const u32x4 a0 = *reinterpret_cast<const u32x4*>(src + k_rd[2 * ks]);
+        const u32x4 a1 = *reinterpret_cast<const u32x4*>(src + k_rd[2 * ks + 1]);
         const i32x8 a = __builtin_bit_cast(i32x8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
         if (ks == 0)
           s[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, qf[ks], s[kb], 0, 0, 0, (int)ksc, 0, qsc);
@@ -304,8 +313,8 @@ struct FwdF8 {
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
       const unsigned char* src = vt + 32 * db * C::vStride;
-      const u32x4 a0 = *reinterpret_cast<const u32x4*>(src);
-      const u32x4 a1 = *reinterpret_cast<const u32x4*>(src + 16);
+      const u32x4 a0 = *reinterpret_cast<const u32x4*>(src + v_rd[0]);
+      const u32x4 a1 = *reinterpret_cast<const u32x4*>(src + v_rd[1]);
       const i32x8 a = __builtin_bit_cast(i32x8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
       if (db == 0)
         acc[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, pf, acc[db], 0, 0, 0, (int)vsc, 0, kUnitScale);
@@ -394,14 +403,23 @@ __global__ __launch_bounds__(kF8Threads, 2) void fwd_fp8_kernel(
     f.qsc = D == 128 ? (int)(((w >> (8 * f.hl)) & 0xFF) | (((w >> (16 + 8 * f.hl)) & 0xFF) << 8))
                      : (int)((w >> (8 * f.hl)) & 0xFF);
   }
+  const auto kswz = [](int r) { return C::kswz(r); };
+  const auto vswz = [](int r) { return C::vswz(r); };
 #pragma unroll
   for (int i = 0; i < C::kDmaPerWave; ++i)
-    f.koff[i] = f8_dma_offset((f.wave + kF8Waves * i) * 64 + lane, C::kStride, D);
+    f.koff[i] = f8_dma_offset((f.wave + kF8Waves * i) * 64 + lane, C::KCH, kswz);
 #pragma unroll
   for (int i = 0; i < C::vDmaPerWave; ++i)
-    f.voff[i] = f8_dma_offset((f.wave + kF8Waves * i) * 64 + lane, C::vStride, kF8Keys);
-  f.k_rd = f.l32 * C::kStride + 16 * f.hl;
-  f.v_rd = f.l32 * C::vStride + 32 * f.hl;
+    f.voff[i] = f8_dma_offset((f.wave + kF8Waves * i) * 64 + lane, C::VCH, vswz);
+  // K row 32 kb + l32 (the swizzle depends on l32 only), logical chunks
+  // 4 ks + hl and 4 ks + 2 + hl; V^T row 32 db + l32, chunks 2 hl, 2 hl + 1
+#pragma unroll
+  for (int ks = 0; ks < F::KS; ++ks)
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      f.k_rd[2 * ks + h] = f.l32 * C::kStride + 16 * ((4 * ks + 2 * h + f.hl) ^ C::kswz(f.l32));
+#pragma unroll
+  for (int h = 0; h < 2; ++h) f.v_rd[h] = f.l32 * C::vStride + 16 * ((2 * f.hl + h) ^ C::vswz(f.l32));
 
   const int kv_end = CAUSAL ? min(N, q0 + BR) : N;
   const int n_tiles = (kv_end + kF8Keys - 1) / kF8Keys;
