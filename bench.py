@@ -6,7 +6,9 @@ One step is one fa_fwd call over the whole workload (all query rows of all
 heads) with Q, K, V already resident in device memory.  W untimed steps are
 followed by K timed steps between two device synchronisations; the kernel's
 own average duration is taken from HIP events recorded on the stream the
-kernel is queued on.  Prints one JSON line.
+kernel is queued on.  Prints one JSON line.  The defaults (300 and 300)
+give the GPU's clock time to settle under the sustained load: a few
+milliseconds of warm-up leave short kernels timed at a lower clock.
 
 Default workload: B=1, H=32, N=16384, d=128, bf16, causal, with 1% of the Q
 and K rows amplified x8.  Throughput counts 4*B*H*N^2*d FLOPs, halved for
@@ -411,8 +413,8 @@ def fp8_bench(fa, args, w, x):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=300)
+    ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--workload", type=int, default=4, help="workload id 1..5")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-bytes", type=int, default=0)
