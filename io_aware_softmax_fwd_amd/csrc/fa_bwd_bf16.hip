@@ -213,7 +213,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(
     const unsigned short* __restrict__ v, const unsigned short* __restrict__ o,
     const unsigned short* __restrict__ dout, const float* __restrict__ lse,
     unsigned short* __restrict__ dq, float* __restrict__ dws, int N, int BH, int n_qtiles,
-    float scale) {
+    float scale, int hg) {
   using F = BwdQ<D, CAUSAL>;
   __shared__ __attribute__((aligned(1024))) unsigned char k_lds0[Dma<D, F::KSTR>::bytes];
   __shared__ __attribute__((aligned(1024))) unsigned char k_lds1[Dma<D, F::KSTR>::bytes];
@@ -222,8 +222,9 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(
   constexpr int KS = D / 16, DB = D / 32, BR = 32 * kBwdWaves;
 
   const int tid = threadIdx.x, lane = tid & 63;
-  const int bh = blockIdx.x % BH;
-  const int qt = n_qtiles - 1 - blockIdx.x / BH;   // heaviest causal tiles first
+  int bh, rank;
+  xcd_order(blockIdx.x, BH, n_qtiles, hg, bh, rank);
+  const int qt = n_qtiles - 1 - rank;   // heaviest causal tiles first
   const int q0 = qt * BR;
   const int64_t head = (int64_t)bh * N * D;
 
@@ -427,7 +428,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
     const unsigned short* __restrict__ q, const unsigned short* __restrict__ k,
     const unsigned short* __restrict__ v, const unsigned short* __restrict__ dout,
     const float* __restrict__ lse, const float* __restrict__ dws, unsigned short* __restrict__ dk,
-    unsigned short* __restrict__ dv, int N, int BH, float scale) {
+    unsigned short* __restrict__ dv, int N, int BH, float scale, int hg) {
   using F = BwdKV<D, CAUSAL>;
   __shared__ __attribute__((aligned(1024))) unsigned char q_lds0[Dma<D, F::STR>::bytes];
   __shared__ __attribute__((aligned(1024))) unsigned char q_lds1[Dma<D, F::STR>::bytes];
@@ -440,8 +441,8 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
   constexpr int DB = D / 32, BK = 32 * kBwdWaves;
 
   const int tid = threadIdx.x, lane = tid & 63;
-  const int bh = blockIdx.x % BH;
-  const int kt = blockIdx.x / BH;     // smallest keys first: they meet the most causal queries
+  int bh, kt;   // smallest keys first: they meet the most causal queries
+  xcd_order(blockIdx.x, BH, (N + BK - 1) / BK, hg, bh, kt);
   const int k0 = kt * BK;
   const int64_t head = (int64_t)bh * N * D;
 
@@ -517,6 +518,7 @@ template <int D, bool CAUSAL>
 hipError_t launch_bwd(const BwdProblem& p, hipStream_t stream) {
   const int BH = p.B * p.H;
   const int n_qtiles = (p.N + 32 * kBwdWaves - 1) / (32 * kBwdWaves);
+  const int hg = xcd_head_group(BH, 1, CAUSAL ? n_qtiles : 0, 1);
   const unsigned short* q = static_cast<const unsigned short*>(p.q);
   const unsigned short* k = static_cast<const unsigned short*>(p.k);
   const unsigned short* v = static_cast<const unsigned short*>(p.v);
@@ -525,13 +527,13 @@ hipError_t launch_bwd(const BwdProblem& p, hipStream_t stream) {
   hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)((int64_t)n_qtiles * BH)),
                      dim3(kBwdThreads), 0, stream, q, k, v,
                      static_cast<const unsigned short*>(p.o), dout, p.lse,
-                     static_cast<unsigned short*>(p.dq), dws, p.N, BH, n_qtiles, p.scale);
+                     static_cast<unsigned short*>(p.dq), dws, p.N, BH, n_qtiles, p.scale, hg);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)((int64_t)n_qtiles * BH)),
                      dim3(kBwdThreads), 0, stream, q, k, v, dout, p.lse, dws,
                      static_cast<unsigned short*>(p.dk), static_cast<unsigned short*>(p.dv), p.N, BH,
-                     p.scale);
+                     p.scale, hg);
   return hipGetLastError();
 }
 

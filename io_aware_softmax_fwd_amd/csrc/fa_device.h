@@ -57,5 +57,23 @@ __device__ __forceinline__ int dma_offset(int slot, int stride) {
   return r * (2 * D) + 16 * cc;
 }
 
+// Block b -> (head, rank of the block among its head's per blocks).  hg > 0
+// needs BH a multiple of 8: blocks are dealt to the eight XCDs in turn (block
+// b to XCD b % 8), each with its own L2, so head h is placed on XCD h % 8 and
+// an XCD takes its heads hg at a time, rank 0 of every head of the group
+// first, then rank 1, ...  The blocks of a group then read the same K/V at
+// about the same time and share it in L2.  hg = 0: heads vary fastest.
+__device__ __forceinline__ void xcd_order(int b, int BH, int per, int hg, int& head, int& rank) {
+  if (hg > 0) {
+    const int xcd = b & 7, s = b >> 3;
+    const int grp = s / (hg * per), r = s % (hg * per);
+    head = xcd + 8 * (grp * hg + r % hg);
+    rank = r / hg;
+  } else {
+    head = b % BH;
+    rank = b / BH;
+  }
+}
+
 }  // namespace
 }  // namespace fa

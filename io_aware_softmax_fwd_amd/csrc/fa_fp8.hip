@@ -342,7 +342,8 @@ __global__ __launch_bounds__(kF8Threads, 2) void fwd_fp8_kernel(
     const unsigned char* __restrict__ q8, const unsigned char* __restrict__ qs,
     const unsigned char* __restrict__ k8, const unsigned char* __restrict__ ks,
     const unsigned char* __restrict__ v8t, const unsigned char* __restrict__ vs,
-    unsigned short* __restrict__ o, float* __restrict__ lse, int N, int BH, int n_qtiles, float scale) {
+    unsigned short* __restrict__ o, float* __restrict__ lse, int N, int BH, int n_qtiles, float scale,
+    int hg) {
   using F = FwdF8<D, CAUSAL>;
   using C = F8Cfg<D>;
   __shared__ __attribute__((aligned(1024))) unsigned char k_lds0[C::kTile];
@@ -353,8 +354,9 @@ __global__ __launch_bounds__(kF8Threads, 2) void fwd_fp8_kernel(
   const int T = (N + kF8Keys - 1) / kF8Keys;
 
   const int tid = threadIdx.x, lane = tid & 63;
-  const int bh = blockIdx.x % BH;
-  const int qt = n_qtiles - 1 - blockIdx.x / BH;   // heaviest causal tiles first
+  int bh, rank;
+  xcd_order(blockIdx.x, BH, n_qtiles, hg, bh, rank);
+  const int qt = n_qtiles - 1 - rank;   // heaviest causal tiles first
   const int q0 = qt * BR;
 
   F f;
@@ -487,7 +489,7 @@ hipError_t launch_fp8(const Fp8Problem& p, hipStream_t stream) {
                      static_cast<const unsigned char*>(p.qs), static_cast<const unsigned char*>(p.k8),
                      static_cast<const unsigned char*>(p.ks), static_cast<const unsigned char*>(p.v8t),
                      static_cast<const unsigned char*>(p.vs), static_cast<unsigned short*>(p.o), p.lse, p.N,
-                     BH, n_qtiles, p.scale);
+                     BH, n_qtiles, p.scale, xcd_head_group(BH, 1, CAUSAL ? n_qtiles : 0, 1));
   return hipGetLastError();
 }
 

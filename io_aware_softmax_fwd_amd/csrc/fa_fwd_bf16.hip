@@ -311,6 +311,7 @@ __device__ __forceinline__ void position_range(int a, int n, int Nq, int& lo, in
 
 // One workgroup per (query tile, key chunk, batch * K/V head).  The query
 // rows of K/V head bkv are rows [bkv*G*Nq, (bkv+1)*G*Nq) of Q, O and LSE.
+// Blocks map to heads and tiles through xcd_order with hg heads per group.
 // tph > 0: tiles stay inside one query head (tph tiles per head, G heads);
 // tph == 0: tiles are packed over the whole block of G*Nq rows.  Without
 // SPLIT the single chunk is every key and O/LSE are written directly; with
@@ -321,7 +322,7 @@ __global__ __launch_bounds__(kThreads, QB == 1 ? 2 : 1) void fwd_bf16_kernel(
     const unsigned short* __restrict__ q, const unsigned short* __restrict__ k,
     const unsigned short* __restrict__ v, unsigned short* __restrict__ o,
     float* __restrict__ lse, int Nq, int Nk, int G, int BHkv, int n_qtiles, int tph,
-    float scale, int splits, float* __restrict__ opart, float* __restrict__ lpart) {
+    float scale, int splits, float* __restrict__ opart, float* __restrict__ lpart, int hg) {
   __shared__ __attribute__((aligned(1024))) unsigned char k_lds0[Cfg<D>::kTile];
   __shared__ __attribute__((aligned(1024))) unsigned char k_lds1[Cfg<D>::kTile];
   __shared__ __attribute__((aligned(1024))) unsigned char v_lds0[Cfg<D>::vTile];
@@ -332,11 +333,9 @@ __global__ __launch_bounds__(kThreads, QB == 1 ? 2 : 1) void fwd_bf16_kernel(
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  // Heaviest query tiles first (causal work grows with the position); K/V
-  // heads vary fastest, so with B*Hkv a multiple of 8 every tile reading one
-  // K/V head lands on the same XCD and shares its L2.
-  const int bkv = blockIdx.x % BHkv;
-  const int rest = blockIdx.x / BHkv;
+  // Heaviest query tiles first (causal work grows with the position).
+  int bkv, rest;   // K/V head and rank of the tile (and chunk) within it
+  xcd_order(blockIdx.x, BHkv, (SPLIT ? splits : 1) * n_qtiles, hg, bkv, rest);
   const int split = SPLIT ? rest % splits : 0;
   const int idx = SPLIT ? rest / splits : rest;
   const int R = G * Nq;                  // query rows per K/V head
@@ -606,7 +605,8 @@ hipError_t launch(const GqaProblem& p, hipStream_t stream) {
     const dim3 grid((unsigned)(t.n_qtiles * BHkv));
     hipLaunchKernelGGL((fwd_bf16_kernel<D, 1, CAUSAL, false>), grid, block, 0, stream, q, k, v,
                        static_cast<unsigned short*>(p.o), p.lse, p.Nq, p.Nk, G, BHkv,
-                       (int)t.n_qtiles, t.tph, p.scale, 1, nullptr, nullptr);
+                       (int)t.n_qtiles, t.tph, p.scale, 1, nullptr, nullptr,
+                       xcd_head_group(BHkv, G, t.tph, 1));
     return hipGetLastError();
   }
   const SplitLayout L = splitkv_layout(p.B, p.H, p.Nq, p.d, p.splits);
@@ -615,7 +615,7 @@ hipError_t launch(const GqaProblem& p, hipStream_t stream) {
   const dim3 grid((unsigned)(t.n_qtiles * p.splits * BHkv));
   hipLaunchKernelGGL((fwd_bf16_kernel<D, 1, CAUSAL, true>), grid, block, 0, stream, q, k, v,
                      nullptr, nullptr, p.Nq, p.Nk, G, BHkv, (int)t.n_qtiles, t.tph, p.scale,
-                     p.splits, opart, lpart);
+                     p.splits, opart, lpart, xcd_head_group(BHkv, G, t.tph, p.splits));
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t rows = (int64_t)p.B * p.H * p.Nq;
