@@ -518,7 +518,7 @@ template <int D, bool CAUSAL>
 hipError_t launch_bwd(const BwdProblem& p, hipStream_t stream) {
   const int BH = p.B * p.H;
   const int n_qtiles = (p.N + 32 * kBwdWaves - 1) / (32 * kBwdWaves);
-  const int hg = xcd_head_group(BH, 1, CAUSAL ? n_qtiles : 0, 1);
+  const int hg = xcd_head_group(BH, n_qtiles, 1, CAUSAL ? n_qtiles : 0, 1);
   const unsigned short* q = static_cast<const unsigned short*>(p.q);
   const unsigned short* k = static_cast<const unsigned short*>(p.k);
   const unsigned short* v = static_cast<const unsigned short*>(p.v);

@@ -606,7 +606,7 @@ hipError_t launch(const GqaProblem& p, hipStream_t stream) {
     hipLaunchKernelGGL((fwd_bf16_kernel<D, 1, CAUSAL, false>), grid, block, 0, stream, q, k, v,
                        static_cast<unsigned short*>(p.o), p.lse, p.Nq, p.Nk, G, BHkv,
                        (int)t.n_qtiles, t.tph, p.scale, 1, nullptr, nullptr,
-                       xcd_head_group(BHkv, G, t.tph, 1));
+                       xcd_head_group(BHkv, t.n_qtiles, G, t.tph, 1));
     return hipGetLastError();
   }
   const SplitLayout L = splitkv_layout(p.B, p.H, p.Nq, p.d, p.splits);
@@ -615,7 +615,7 @@ hipError_t launch(const GqaProblem& p, hipStream_t stream) {
   const dim3 grid((unsigned)(t.n_qtiles * p.splits * BHkv));
   hipLaunchKernelGGL((fwd_bf16_kernel<D, 1, CAUSAL, true>), grid, block, 0, stream, q, k, v,
                      nullptr, nullptr, p.Nq, p.Nk, G, BHkv, (int)t.n_qtiles, t.tph, p.scale,
-                     p.splits, opart, lpart, xcd_head_group(BHkv, G, t.tph, p.splits));
+                     p.splits, opart, lpart, xcd_head_group(BHkv, t.n_qtiles, G, t.tph, p.splits));
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t rows = (int64_t)p.B * p.H * p.Nq;

@@ -82,16 +82,18 @@ inline int64_t fp8_v_scale_bytes(int64_t BH, int N, int d) { return BH * ((N + 6
 // Query rows per workgroup tile of the bf16 kernel.
 constexpr int kTileRows = 128;
 
-// Heads an XCD runs at a time in the block order of xcd_order (0 when BH, the
-// number of K/V heads over the batch, is not a multiple of 8).  One at a time
-// reads the least from memory, but a group's last blocks start late, so its
-// heaviest block must stay short next to the time a group takes.  Causal
-// query tiles (tph > 0 per query head, G query heads per K/V head) weigh
-// 1..tph, so the heaviest of `splits` key chunks is tph/splits of a head's
-// G*tph^2/2; an XCD holds 64 workgroups at once (32 CUs, two each).  The
-// group is sized so the heaviest block takes at most half of a group's time.
-inline int xcd_head_group(int64_t BH, int G, int tph, int splits) {
-  if (BH % 8 != 0) return 0;
+// Heads an XCD runs at a time in the block order of xcd_order (0, heads
+// varying fastest, when BH, the number of K/V heads over the batch, is not a
+// multiple of 8, or when a head has a single query tile, so that no two
+// blocks read the same keys).  One at a time reads the least from memory, but
+// a group's last blocks start late, so its heaviest block must stay short
+// next to the time a group takes.  Causal query tiles (tph > 0 per query
+// head, G query heads per K/V head) weigh 1..tph, so the heaviest of `splits`
+// key chunks is tph/splits of a head's G*tph^2/2; an XCD holds 64 workgroups
+// at once (32 CUs, two each).  The group is sized so the heaviest block takes
+// at most half of a group's time.
+inline int xcd_head_group(int64_t BH, int64_t qtiles, int G, int tph, int splits) {
+  if (BH % 8 != 0 || qtiles <= 1) return 0;
   const int hx = (int)(BH / 8);   // heads per XCD
   if (tph == 0) return 1;         // equal tiles
   constexpr int64_t kXcdSlots = 64;
