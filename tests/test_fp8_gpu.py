@@ -217,3 +217,33 @@ def test_fp8_workload_shapes(cfg):
     _, deq = _oracle_quant(x["q"], x["k"], x["v"])
     rows = W.sample_rows(w, 256, seed=cfg + 50)
     _check_rows(O, L, deq, w.scale, w.causal, rows, "C%d" % cfg)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp8_offset_moves(d, causal):
+    """Keys whose score against every query sits far above all earlier keys
+    (by 69, 173 and 231 log2 units; one on the ragged last tile) and one far
+    below: the row max passes the exponent offset by far more than the
+    8-unit headroom on those tiles, so the offset moves there mid-row and
+    the accumulators are rescaled before the probabilities are rounded to
+    E4M3."""
+    torch_or_skip()
+    H, N = 2, 700
+    case = "fp8 offset moves N=%d d=%d causal=%d" % (N, d, causal)
+    note(case)
+    rng = np.random.default_rng(9300 + d + causal)
+    q = rng.standard_normal((1, H, N, d), dtype=np.float32) * 0.5
+    k = rng.standard_normal((1, H, N, d), dtype=np.float32) * 0.1
+    v = rng.standard_normal((1, H, N, d), dtype=np.float32)
+    q[..., 0] = 4.0
+    k[..., 0] = 0.0
+    k[:, :, 200, 0] = 12.0
+    k[:, :, 500, 0] = 30.0
+    k[:, :, N - 3, 0] = 40.0
+    k[:, :, 100, 0] = -30.0
+    rt = lambda x: W.bf16_bits_to_f32(W.bf16_bits_rne(x))
+    q, k, v = rt(q), rt(k), rt(v)
+    O, L = _run_fp8(*_gpu_quant(q, k, v), 1.0, causal)
+    _, deq = _oracle_quant(q, k, v)
+    _check_rows(O, L, deq, 1.0, causal, np.arange(H * N), case)
