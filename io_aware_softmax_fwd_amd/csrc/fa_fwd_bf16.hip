@@ -35,7 +35,7 @@
 // head-dim block, plus compile-time offsets.
 // Rescaling is lazy and needs no row max on most tiles: a tile's
 // probabilities are first taken against the current offset m; they are kept
-// when no lane's share of their sum exceeds 2^32 (so no probability does
+// when no lane's share of their sum exceeds 2^48 (so no probability does
 // either).  Only otherwise (a row's first tile, where m = -inf, or a score far
 // above m) is the row max taken, m moved to it, the accumulator rescaled by
 // exp(m_old - m_new) and the probabilities redone.  Since O and l share the
@@ -62,9 +62,11 @@ constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kKeys = 64;                 // keys per K/V tile (Bc)
 // A tile's probabilities against a stale offset are kept while every lane's
-// share of their sum (32 of them) is at most this, so a row sum grows by at
-// most 2^27 per key: far from the fp32 range limit.
-constexpr float kProbSumMax = 4294967296.0f;
+// share of their sum (32 of them) is at most this, so no kept probability
+// exceeds 2^48: with fewer than 2^31 keys the accumulators stay below
+// 2^79 max|v|, far from the fp32 range limit for any V a bf16 caller has
+// short of 2^49.
+constexpr float kProbSumMax = 0x1p48f;
 
 template <int D> struct Cfg {
   // Rows are stored unpadded (2*D bytes); each row's 16-byte chunks are

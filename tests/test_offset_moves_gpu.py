@@ -3,7 +3,7 @@
 The bf16 kernels take a tile's probabilities against the row's current
 offset and move the offset (to the tile's row max, rescaling what was
 accumulated) only when some lane's share of the tile's probability sum
-exceeds 2^32 or is not finite.  These inputs force that move on chosen
+exceeds 2^48 or is not finite.  These inputs force that move on chosen
 tiles: keys whose score against every query sits far above all earlier
 keys (by 69, 173 and 231 log2 units), one on a ragged last tile, and a key far
 below the rest.  Results must still match the fp64 oracle at the bf16
