@@ -100,6 +100,7 @@ struct Fwd {
   int wave, l32, hl;
   int pos[QB];            // position inside its head of this lane's query, per block
   int wlast;              // causal: last key any valid query of this wave sees (-1: none)
+  bool rows;              // the wave has a valid query row
   float c;                // scale * log2(e)
   bf16x8 qf[QB][KS];      // Q fragments (B operand of S^T = K Q^T), per 32-row block
   f32x16 acc[QB][DB];     // O^T accumulators: lane holds query l%32 of each block
@@ -290,8 +291,9 @@ struct Fwd {
       issue<true, PAR ^ 1>(k0 + kKeys);
     }
     // Causal: a wave whose last query precedes the tile's first key has
-    // nothing to do here or later; the barrier below stays unconditional.
-    if (!MASK || !CAUSAL || k0 <= wlast) consume<MASK, PAR>(k0);
+    // nothing to do here or later; key chunks of a decoding step leave whole
+    // waves without a query row.  The barrier below stays unconditional.
+    if ((!SPLIT || rows) && (!MASK || !CAUSAL || k0 <= wlast)) consume<MASK, PAR>(k0);
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
     __builtin_amdgcn_s_barrier();
   }
@@ -368,6 +370,7 @@ __global__ __launch_bounds__(kThreads, QB == 1 ? 2 : 1) void fwd_bf16_kernel(
   {
     const int w0 = f.wave * F::WR;       // first row of this wave in the tile
     int lo, hi;
+    f.rows = w0 < nr;
     if (w0 < nr) {
       position_range(r0 + w0, min(F::WR, nr - w0), Nq, lo, hi);
       f.wlast = hi + f.coff;
