@@ -432,7 +432,7 @@ def main():
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build runs on one GPU only; the forward pass shards by "
+        print("bench.py: the benchmark runs on one GPU only; the forward pass shards by "
               "(batch, head) with no communication, so --gpus must be 1.", file=sys.stderr)
         sys.exit(2)
 
