@@ -64,7 +64,7 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 matrix-core peak (published)
 PEAK_FP8_TFLOPS = 5000.0        # MI355X dense fp8 matrix-core peak (published)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fa_fwd_bf16_traffic.json")
-KERNEL_SOURCES = ["fa_fwd_bf16.hip", "fa_internal.h", "fa_api.cpp"]
+KERNEL_SOURCES = ["fa_fwd_bf16.hip", "fa_device.h", "fa_internal.h", "fa_api.cpp"]
 
 
 def kernel_source_hash():
