@@ -51,7 +51,7 @@ enum fa_status {
   FA_ERR_CAUSAL = 7,         /* causal flag other than 0 or 1                  */
   FA_ERR_ALIAS = 8,          /* an output or the workspace overlaps a buffer   */
   FA_ERR_WORKSPACE = 9,      /* workspace NULL or smaller than required        */
-  FA_ERR_SPLITS = 10,        /* num_splits outside 1..128                      */
+  FA_ERR_SPLITS = 10,        /* num_splits outside 1..256                      */
   FA_ERR_HEADS = 11          /* H is not a multiple of Hkv                     */
 };
 
@@ -98,7 +98,7 @@ int fa_fwd_f32(const float* q, const float* k, const float* v, float* o,
  *   Nq, Nk    : query rows and keys, >= 1.  Causal aligns the last query with
  *               the last key: query i attends keys j <= i + Nk - Nq, so causal
  *               calls need Nq <= Nk (Nq == Nk is the square problem).
- *   num_splits: 1..128 chunks (fa_fwd_splitkv_num_splits suggests one).
+ *   num_splits: 1..256 chunks (fa_fwd_splitkv_num_splits suggests one).
  *   workspace : device buffer of at least fa_fwd_splitkv_workspace_size(...)
  *               bytes, 16-byte aligned, owned by the caller, overlapping no
  *               other argument; its contents are scratch (nothing is kept
@@ -118,9 +118,11 @@ int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* 
  * argument is out of range.  Host only, no HIP call. */
 size_t fa_fwd_splitkv_workspace_size(int B, int H, int Nq, int d, int num_splits);
 
-/* A chunk count that gives about four workgroups per CU on a GPU with
- * num_cus compute units (<= 0 means 256), keeping chunks of at least four
- * 64-key tiles.  Host only, no HIP call. */
+/* A chunk count for a GPU with num_cus compute units (<= 0 means 256): two
+ * workgroups per CU when chunks keep at least sixteen 64-key tiles (up to
+ * four per CU while they still do); else, if that takes at most 128 chunks,
+ * two per CU with chunks of at least 4 tiles; else one per CU with chunks of
+ * 8 tiles, or of 4 when the keys are fewer.  Host only, no HIP call. */
 int fa_fwd_splitkv_num_splits(int B, int H, int Nq, int Nk, int num_cus);
 
 /*
@@ -136,7 +138,7 @@ int fa_fwd_splitkv_num_splits(int B, int H, int Nq, int Nk, int num_cus);
  *               and needs Nq <= Nk.  The H/Hkv query heads of a K/V head
  *               must hold fewer than 2^31 rows together.
  *   num_splits: 1 -> one pass, O and LSE written directly, workspace ignored
- *               (may be NULL); 2..128 -> the keys are cut into chunks merged
+ *               (may be NULL); 2..256 -> the keys are cut into chunks merged
  *               as in fa_fwd_splitkv, with a workspace of at least
  *               fa_fwd_splitkv_workspace_size(B, H, Nq, d, num_splits) bytes
  *               (the partials are per query row).

@@ -18,7 +18,7 @@ namespace {
 // Largest supported problem: element offsets stay far inside int64 and the
 // 1-D grid (query tiles x heads) inside 2^31 workgroups.
 constexpr int64_t kMaxElems = int64_t(1) << 40;
-constexpr int kMaxSplits = 128;
+constexpr int kMaxSplits = 256;
 
 bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
 
@@ -91,15 +91,34 @@ int validate_gqa(const void* q, const void* k, const void* v, const void* o, con
   return FA_OK;
 }
 
-// About four workgroups per CU (two resident, two queued), keeping at least
-// four 64-key tiles per chunk.
+// Chunks per row block, from the workgroups one chunk level gives (base) and
+// the 64-key tiles of a row (tiles).  Measured on decoding with 1 to 32 K/V
+// heads over 4K to 128K keys: a chunk streams best at 16 or more tiles, the
+// GPU fills at two workgroups per CU, and a merge over hundreds of chunks per
+// row costs more than it saves.  So: two workgroups per CU when chunks keep
+// 16 tiles (doubling up to four per CU while they still do); else, when that
+// takes at most 128 chunks, two per CU with chunks of at least 4 tiles;
+// else one per CU, with chunks of 8 tiles if the keys allow, else of 4.
 int choose_splits(int B, int H, int Hkv, int Nq, int Nk, int causal, int num_cus) {
   if (B < 1 || H < 1 || Hkv < 1 || H % Hkv != 0 || Nq < 1 || Nk < 1) return 1;
   if (num_cus < 1) num_cus = 256;
   const int64_t base = fa::query_tiling(H / Hkv, Nq, causal != 0).n_qtiles * B * Hkv;
-  const int64_t want = ((int64_t)4 * num_cus + base - 1) / base;
-  const int64_t most = std::max<int64_t>(1, ((Nk + 63) / 64) / 4);
-  return (int)std::max<int64_t>(1, std::min<int64_t>(std::min<int64_t>(want, most), kMaxSplits));
+  const int64_t tiles = (Nk + 63) / 64;
+  const int64_t s1 = (num_cus + base - 1) / base;
+  const int64_t s2 = (2 * (int64_t)num_cus + base - 1) / base;
+  const int64_t s4 = (4 * (int64_t)num_cus + base - 1) / base;
+  int64_t s;
+  if (tiles >= 16 * s2) {
+    s = s2;
+    while (2 * s <= s4 && tiles >= 16 * 2 * s) s *= 2;
+  } else if (s2 <= 128) {
+    s = std::min<int64_t>(s2, tiles / 4);
+  } else if (tiles >= 8 * s1) {
+    s = s1;
+  } else {
+    s = std::min<int64_t>(s1, tiles / 4);
+  }
+  return (int)std::max<int64_t>(1, std::min<int64_t>(s, kMaxSplits));
 }
 
 int validate_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
@@ -280,7 +299,7 @@ const char* fa_strerror(int status) {
     case FA_ERR_CAUSAL: return "causal must be 0 or 1";
     case FA_ERR_ALIAS: return "an output or the workspace overlaps another buffer";
     case FA_ERR_WORKSPACE: return "workspace missing or smaller than the size query returns";
-    case FA_ERR_SPLITS: return "num_splits must be between 1 and 128";
+    case FA_ERR_SPLITS: return "num_splits must be between 1 and 256";
     case FA_ERR_HEADS: return "H must be a multiple of Hkv";
     default: return "unknown status";
   }

@@ -109,7 +109,7 @@ def _split_call(**kw):
     (dict(causal=1, Nq=129, Nk=128), fa.FA_ERR_SHAPE),
     (dict(d=80), fa.FA_ERR_UNSUPPORTED_D), (dict(scale=-1.0), fa.FA_ERR_SCALE),
     (dict(causal=3), fa.FA_ERR_CAUSAL),
-    (dict(splits=0), fa.FA_ERR_SPLITS), (dict(splits=129), fa.FA_ERR_SPLITS),
+    (dict(splits=0), fa.FA_ERR_SPLITS), (dict(splits=257), fa.FA_ERR_SPLITS),
     (dict(ws=None), fa.FA_ERR_WORKSPACE), (dict(ws_bytes=100), fa.FA_ERR_WORKSPACE),
     (dict(ws=A + 64 * MB + 8), fa.FA_ERR_ALIGN), (dict(v=A + 16 * MB + 4), fa.FA_ERR_ALIGN),
     (dict(ws=A + 24 * MB), fa.FA_ERR_ALIAS), (dict(o=A + 8 * MB), fa.FA_ERR_ALIAS),
@@ -127,8 +127,18 @@ def test_splitkv_workspace_size_and_split_choice():
     assert fa.fa_fwd_splitkv_workspace_size(1, 1, 1, 64, 0) == 0
     # big grids need no split; small grids and long key runs get more
     assert fa.fa_fwd_splitkv_num_splits(1, 32, 16384, 16384, 256) == 1
+    # 128 row blocks of 16 tiles: two workgroups per CU, chunks of 4 tiles
     assert fa.fa_fwd_splitkv_num_splits(2, 8, 1024, 1024, 256) == 4
-    assert fa.fa_fwd_splitkv_num_splits(1, 8, 1, 32768, 256) == 128
+    # decoding 8 heads over 512 tiles: two per CU, 64 chunks of 8 tiles
+    assert fa.fa_fwd_splitkv_num_splits(1, 8, 1, 32768, 256) == 64
+    # 32 heads over 2048 tiles: two per CU (16 chunks), doubled while chunks keep 16 tiles
+    assert fa.fa_fwd_splitkv_num_splits(1, 32, 1, 131072, 256) == 32
+    assert fa.fa_fwd_splitkv_num_splits(1, 32, 1, 32768, 256) == 32
+    assert fa.fa_fwd_splitkv_num_splits(1, 32, 1, 4096, 256) == 16
+    # one head over 2048 tiles: one per CU, chunks of 8 tiles
+    assert fa.fa_fwd_splitkv_num_splits(1, 1, 1, 131072, 256) == 256
+    # one head over 512 tiles: chunks of 4 tiles at most
+    assert fa.fa_fwd_splitkv_num_splits(1, 1, 1, 32768, 256) == 128
     assert fa.fa_fwd_splitkv_num_splits(1, 1, 1, 64, 256) == 1
 
 
@@ -152,7 +162,7 @@ def _gqa_call(**kw):
     (dict(H=1 << 12, Hkv=1, Nq=1 << 19, Nk=1 << 19, splits=1), fa.FA_ERR_SHAPE),
     (dict(d=32), fa.FA_ERR_UNSUPPORTED_D), (dict(scale=0.0), fa.FA_ERR_SCALE),
     (dict(causal=2), fa.FA_ERR_CAUSAL),
-    (dict(splits=0), fa.FA_ERR_SPLITS), (dict(splits=200), fa.FA_ERR_SPLITS),
+    (dict(splits=0), fa.FA_ERR_SPLITS), (dict(splits=300), fa.FA_ERR_SPLITS),
     (dict(ws=None), fa.FA_ERR_WORKSPACE), (dict(ws_bytes=64), fa.FA_ERR_WORKSPACE),
     (dict(ws=A + 64 * MB + 4), fa.FA_ERR_ALIGN), (dict(lse=A + 32 * MB + 8), fa.FA_ERR_ALIGN),
     (dict(ws=A + 8 * MB), fa.FA_ERR_ALIAS), (dict(lse=A + 16 * MB), fa.FA_ERR_ALIAS),
@@ -166,7 +176,10 @@ def test_gqa_bad_arguments_rejected_on_host(kw, status):
 
 def test_gqa_split_choice():
     # grouped heads of a decoding step share one tile per K/V head
-    assert fa.fa_fwd_gqa_num_splits(1, 32, 8, 1, 32768, 1, 256) == 128
+    assert fa.fa_fwd_gqa_num_splits(1, 32, 8, 1, 32768, 1, 256) == 64
+    assert fa.fa_fwd_gqa_num_splits(1, 32, 8, 1, 131072, 1, 256) == 128
+    assert fa.fa_fwd_gqa_num_splits(1, 32, 2, 1, 131072, 1, 256) == 128
+    assert fa.fa_fwd_gqa_num_splits(1, 32, 1, 1, 131072, 1, 256) == 256
     assert fa.fa_fwd_gqa_num_splits(1, 32, 8, 1, 2048, 1, 256) == 8
     # Hkv == H agrees with the multi-head choice
     for args in ((2, 8, 1024, 1024), (1, 8, 1, 32768), (1, 32, 16384, 16384), (3, 5, 77, 900)):
