@@ -1,6 +1,6 @@
 // bf16 attention forward on the gfx950 matrix cores.
 //
-// One workgroup owns 128 query rows of one (batch, head) and streams the K/V
+// One workgroup owns 128 (or 256) query rows of one (batch, head) and streams the K/V
 // tiles of that head through LDS; the scores and probabilities of a tile live
 // only in registers and are merged into a running row max m, row sum l and an
 // unnormalised fp32 accumulator, which is rescaled by exp(m_old - m_new) when
@@ -9,7 +9,8 @@
 // write-up, sections 3.2 and 4.3).  Queries are the outer loop and keys the
 // inner one, so a query tile reads Q once and writes O once.
 //
-// Work inside a workgroup (4 waves of 64 lanes, 32 query rows per wave):
+// Work inside a workgroup (4 waves of 64 lanes, 32 query rows per wave, or
+// two blocks of 32 when d = 64 and the grid is large; see launch):
 //   * scores are produced transposed, S^T = K Q^T, by
 //     v_mfma_f32_32x32x16_bf16 with K (from LDS) as the A operand and Q
 //     (registers, loaded once) as the B operand.  In the accumulator layout
@@ -322,7 +323,7 @@ __device__ __forceinline__ void position_range(int a, int n, int Nq, int& lo, in
 // SPLIT the chunk's own normalised O (fp32) and LSE go to opart/lpart for
 // the merge.
 template <int D, int QB, bool CAUSAL, bool SPLIT>
-__global__ __launch_bounds__(kThreads, QB == 1 ? 2 : 1) void fwd_bf16_kernel(
+__global__ __launch_bounds__(kThreads, (QB == 1 || D == 64) ? 2 : 1) void fwd_bf16_kernel(
     const unsigned short* __restrict__ q, const unsigned short* __restrict__ k,
     const unsigned short* __restrict__ v, unsigned short* __restrict__ o,
     float* __restrict__ lse, int Nq, int Nk, int G, int BHkv, int n_qtiles, int tph,
@@ -594,6 +595,8 @@ __global__ __launch_bounds__(256) void merge_rows_kernel(const float* __restrict
 
 // Rows above which the merge runs one thread per (row, 8 dims).
 constexpr int64_t kMergeRowsMin = 4096;
+// Workgroups from which d = 64 takes 256-row tiles: two per CU of the 256.
+constexpr int64_t kWideTileMinGrid = 512;
 
 template <int D, bool CAUSAL>
 hipError_t launch(const GqaProblem& p, hipStream_t stream) {
@@ -606,6 +609,24 @@ hipError_t launch(const GqaProblem& p, hipStream_t stream) {
   const unsigned short* q = static_cast<const unsigned short*>(p.q);
   const unsigned short* k = static_cast<const unsigned short*>(p.k);
   const unsigned short* v = static_cast<const unsigned short*>(p.v);
+  // d = 64 leaves half the registers free at 32 rows per wave: 64 rows per
+  // wave (two 32-row blocks sharing every K and V fragment read) halve the
+  // LDS reads and the L2-to-LDS bytes per product, and still fit two
+  // workgroups per CU.  Taken when the 256-row tiles give at least two
+  // workgroups per CU of the 256.
+  if constexpr (D == 64) {
+    if (p.splits == 1) {
+      const QueryTiling t2 = query_tiling(G, p.Nq, p.causal, 2 * BR);
+      if (t2.n_qtiles * BHkv >= kWideTileMinGrid) {
+        const dim3 grid((unsigned)(t2.n_qtiles * BHkv));
+        hipLaunchKernelGGL((fwd_bf16_kernel<D, 2, CAUSAL, false>), grid, block, 0, stream, q, k, v,
+                           static_cast<unsigned short*>(p.o), p.lse, p.Nq, p.Nk, G, BHkv,
+                           (int)t2.n_qtiles, t2.tph, p.scale, 1, nullptr, nullptr,
+                           xcd_head_group(BHkv, t2.n_qtiles, G, t2.tph, 1));
+        return hipGetLastError();
+      }
+    }
+  }
   if (p.splits == 1) {
     const dim3 grid((unsigned)(t.n_qtiles * BHkv));
     hipLaunchKernelGGL((fwd_bf16_kernel<D, 1, CAUSAL, false>), grid, block, 0, stream, q, k, v,

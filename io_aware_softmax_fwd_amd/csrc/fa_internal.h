@@ -112,14 +112,14 @@ struct QueryTiling {
   int tph;
   int64_t n_qtiles;   // tiles per K/V head
 };
-inline QueryTiling query_tiling(int G, int Nq, int causal) {
+inline QueryTiling query_tiling(int G, int Nq, int causal, int rows = kTileRows) {
   QueryTiling t;
-  if (causal && Nq >= kTileRows) {
-    t.tph = (Nq + kTileRows - 1) / kTileRows;
+  if (causal && Nq >= rows) {
+    t.tph = (Nq + rows - 1) / rows;
     t.n_qtiles = (int64_t)G * t.tph;
   } else {
     t.tph = 0;
-    t.n_qtiles = ((int64_t)G * Nq + kTileRows - 1) / kTileRows;
+    t.n_qtiles = ((int64_t)G * Nq + rows - 1) / rows;
   }
   return t;
 }

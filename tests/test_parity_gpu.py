@@ -162,3 +162,19 @@ def test_no_writes_outside_outputs(dtype):
     assert np.all(ob[:pad] == 7.0) and np.all(ob[pad + B * H * N * d:] == 7.0)
     assert np.all(lb[:pad] == 7.0) and np.all(lb[pad + B * H * N:] == 7.0)
     assert np.all(np.isfinite(ob[pad:pad + B * H * N * d]))
+
+
+# ------------------------------------------- d = 64 with 256-row tiles
+@pytest.mark.parametrize("B,H,N,causal", [(1, 64, 2000, True), (2, 32, 1900, False)])
+def test_d64_wide_tiles_full(B, H, N, causal):
+    """d = 64 problems with at least 512 tiles of 256 rows run two 32-row
+    blocks per wave; ragged last tiles, causal diagonals, every row against
+    the oracle."""
+    torch_or_skip()
+    d = 64
+    note("d=64 wide tiles: B=%d H=%d N=%d causal=%d" % (B, H, N, causal))
+    q, k, v = (_as(_rand((B, H, N, d), 600 + N + t), "bf16") for t in range(3))
+    scale = float(np.float32(1 / math.sqrt(d)))
+    O, L = run(q, k, v, scale, causal, "bf16")
+    O_ref, L_ref = oracle.attention_c(q, k, v, scale, causal)
+    assert_close(O, L, O_ref, L_ref, "bf16", "d=64 wide tiles B=%d H=%d N=%d causal=%d" % (B, H, N, causal))
