@@ -55,6 +55,8 @@ CASES = [
     (1, 2, 2, 130, 130, 128, True, 1),      # one query head per K/V head
     (1, 4, 1, 1, 1, 64, True, 1),
     (1, 4, 4, 3, 70, 128, True, 2),
+    (1, 64, 16, 2048, 2048, 64, True, 1),   # d = 64, 512 tiles of 256 rows: two blocks per wave
+    (2, 64, 8, 1000, 1000, 64, False, 1),   # the same, packed 256-row tiles crossing heads
 ]
 
 
@@ -76,7 +78,8 @@ def test_gqa_matches_oracle(B, H, Hkv, Nq, Nk, d, causal, splits):
 
 
 @pytest.mark.parametrize("H,Hkv,Nq,Nk,causal", [
-    (8, 2, 50, 700, True), (8, 2, 300, 300, True), (8, 4, 200, 333, False), (16, 1, 1, 2000, True)])
+    (8, 2, 50, 700, True), (8, 2, 300, 300, True), (8, 4, 200, 333, False), (16, 1, 1, 2000, True),
+    (64, 8, 1000, 1000, False)])
 def test_gqa_equals_multihead_on_repeated_heads(H, Hkv, Nq, Nk, causal):
     """One pass (no key split) gives every query row the same key tiles in
     the same order whichever rows share its workgroup, so fa_fwd_gqa must
