@@ -62,8 +62,9 @@ enum fa_status {
  *             even from the fp32 result).
  *   lse     : device pointer, [B,H,N] float32, written.
  *   B, H, N : batch, heads, sequence length (N >= 1; any N, no tile multiple
- *             needed).  B*H*N*d must stay below 2^40 elements and one head
- *             (N*d elements) below 2 GiB.
+ *             needed).  B*H*N*d must stay below 2^40 elements,
+ *             B*H*ceil(N/32) (a bound of the workgroup count) below 2^31
+ *             and one head (N*d elements) below 2 GiB.
  *   d       : head dimension, 64 or 128.
  *   scale   : multiplier of Q K^T before the softmax, finite and > 0
  *             (usually 1/sqrt(d)).

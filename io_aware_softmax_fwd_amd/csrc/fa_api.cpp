@@ -22,6 +22,13 @@ constexpr int kMaxSplits = 256;
 
 bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
 
+// Workgroup count bound of the square problems: no launch takes more than
+// one workgroup per 32 query rows of a head, and the kernels index heads and
+// workgroups with 32-bit integers.
+bool grid_too_large(int64_t heads, int64_t rows_per_head) {
+  return heads * ((rows_per_head + 31) / 32) >= (int64_t(1) << 31);
+}
+
 bool overlap(const void* a, int64_t a_bytes, const void* b, int64_t b_bytes) {
   const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
   return a0 < b0 + (uintptr_t)b_bytes && b0 < a0 + (uintptr_t)a_bytes;
@@ -33,7 +40,7 @@ int validate(const void* q, const void* k, const void* v, const void* o, const f
   if (B < 1 || H < 1 || N < 1) return FA_ERR_SHAPE;
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED_D;
   const int64_t rows = (int64_t)B * H * N;
-  if (rows * d >= kMaxElems) return FA_ERR_SHAPE;
+  if (rows * d >= kMaxElems || grid_too_large((int64_t)B * H, N)) return FA_ERR_SHAPE;
   // One head's K or V (N x d) must stay below 2 GiB: the kernels address a
   // head with 32-bit byte offsets.
   if ((int64_t)N * d * elem_bytes >= (int64_t(1) << 31)) return FA_ERR_SHAPE;
@@ -128,7 +135,7 @@ int validate_bwd(const void* q, const void* k, const void* v, const void* o, con
   if (B < 1 || H < 1 || N < 1) return FA_ERR_SHAPE;
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED_D;
   const int64_t rows = (int64_t)B * H * N;
-  if (rows * d >= kMaxElems) return FA_ERR_SHAPE;
+  if (rows * d >= kMaxElems || grid_too_large((int64_t)B * H, N)) return FA_ERR_SHAPE;
   if ((int64_t)N * d * 2 >= (int64_t(1) << 31)) return FA_ERR_SHAPE;
   if (!(scale > 0.f) || !isfinite(scale)) return FA_ERR_SCALE;
   if (causal != 0 && causal != 1) return FA_ERR_CAUSAL;
@@ -274,7 +281,8 @@ int fa_fwd_fp8(const void* q8, const void* qs, const void* k8, const void* ks, c
   if (B < 1 || H < 1 || N < 1) return FA_ERR_SHAPE;
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED_D;
   const int64_t rows = (int64_t)B * H * N;
-  if (rows * d >= kMaxElems || (int64_t)N * d * 2 >= (int64_t(1) << 31)) return FA_ERR_SHAPE;
+  if (rows * d >= kMaxElems || (int64_t)N * d * 2 >= (int64_t(1) << 31) || grid_too_large((int64_t)B * H, N))
+    return FA_ERR_SHAPE;
   if (!(scale > 0.f) || !isfinite(scale)) return FA_ERR_SCALE;
   if (causal != 0 && causal != 1) return FA_ERR_CAUSAL;
   if (any_misaligned({q8, qs, k8, ks, v8t, vs, o, lse})) return FA_ERR_ALIGN;
@@ -291,7 +299,7 @@ const char* fa_strerror(int status) {
   switch (status) {
     case FA_OK: return "success";
     case FA_ERR_NULL: return "a required pointer is NULL";
-    case FA_ERR_SHAPE: return "B, H, N must be >= 1, B*H*N*d below 2^40 and one head below 2 GiB";
+    case FA_ERR_SHAPE: return "B, H, N must be >= 1, B*H*N*d below 2^40, B*H*ceil(N/32) below 2^31 and one head below 2 GiB";
     case FA_ERR_UNSUPPORTED_D: return "head dimension must be 64 or 128";
     case FA_ERR_SCALE: return "scale must be finite and > 0";
     case FA_ERR_ALIGN: return "pointers must be 16-byte aligned";

@@ -60,6 +60,9 @@ def _call(fn, **kw):
     (dict(B=0), fa.FA_ERR_SHAPE), (dict(H=-1), fa.FA_ERR_SHAPE), (dict(N=0), fa.FA_ERR_SHAPE),
     (dict(B=1 << 20, H=1 << 10, N=1 << 10, d=128), fa.FA_ERR_SHAPE),
     (dict(N=1 << 23, d=128), fa.FA_ERR_SHAPE),
+    # 2^31 heads of one row: 2^37 elements, but one workgroup per head
+    (dict(B=1 << 16, H=1 << 15, N=1, d=64), fa.FA_ERR_SHAPE),
+    (dict(B=1 << 16, H=1 << 15, N=7, d=64), fa.FA_ERR_SHAPE),
     (dict(d=32), fa.FA_ERR_UNSUPPORTED_D), (dict(d=96), fa.FA_ERR_UNSUPPORTED_D),
     (dict(d=256), fa.FA_ERR_UNSUPPORTED_D),
     (dict(scale=0.0), fa.FA_ERR_SCALE), (dict(scale=-0.5), fa.FA_ERR_SCALE),
@@ -211,6 +214,7 @@ def _bwd_call(**kw):
     (dict(dq=None), fa.FA_ERR_NULL), (dict(dv=None), fa.FA_ERR_NULL),
     (dict(B=0), fa.FA_ERR_SHAPE), (dict(N=0), fa.FA_ERR_SHAPE),
     (dict(N=1 << 23, d=128), fa.FA_ERR_SHAPE),
+    (dict(B=1 << 16, H=1 << 15, N=1, d=64), fa.FA_ERR_SHAPE),
     (dict(d=96), fa.FA_ERR_UNSUPPORTED_D), (dict(scale=float("nan")), fa.FA_ERR_SCALE),
     (dict(causal=5), fa.FA_ERR_CAUSAL),
     (dict(dk=A + 56 * MB + 2), fa.FA_ERR_ALIGN), (dict(ws=A + 72 * MB + 8), fa.FA_ERR_ALIGN),
@@ -261,6 +265,7 @@ def test_fp8_v_sizes():
 @pytest.mark.parametrize("kw,status", [
     (dict(q8=None), fa.FA_ERR_NULL), (dict(vs=None), fa.FA_ERR_NULL), (dict(lse=None), fa.FA_ERR_NULL),
     (dict(N=0), fa.FA_ERR_SHAPE), (dict(d=256), fa.FA_ERR_UNSUPPORTED_D),
+    (dict(B=1 << 16, H=1 << 15, N=1), fa.FA_ERR_SHAPE),
     (dict(scale=-1.0), fa.FA_ERR_SCALE), (dict(causal=3), fa.FA_ERR_CAUSAL),
     (dict(ks=A + 24 * MB + 1), fa.FA_ERR_ALIGN), (dict(o=A + 8 * MB), fa.FA_ERR_ALIAS),
     (dict(lse=A + 40 * MB + 16), fa.FA_ERR_ALIAS), (dict(lse=A + 48 * MB), fa.FA_ERR_ALIAS),
