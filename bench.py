@@ -151,6 +151,8 @@ PROFILE_STEPS = {
                   "-- python bench.py --decode 131072 --hkv 8",
     "decode_mha": "rocprofv3 --kernel-trace --stats --output-format csv -d $OUT/decode_mha -o run "
                   "-- python bench.py --decode 131072",
+    "decode_mqa": "rocprofv3 --kernel-trace --stats --output-format csv -d $OUT/decode_mqa -o run "
+                  "-- python bench.py --decode 131072 --hkv 1",
     "bwd": "rocprofv3 --kernel-trace --stats --output-format csv -d $OUT/bwd -o run "
            "-- python bench.py --bwd",
     "fp8": "rocprofv3 --kernel-trace --stats --output-format csv -d $OUT/fp8 -o run "
@@ -161,6 +163,7 @@ PROFILE_STEPS = {
 # extra kernel-trace steps summarised kernel by kernel: step -> summary name
 TRACE_ONLY = {"decode_gqa": "fa_fwd_gqa_decode_b1_h32_hkv8_nk131072_d128",
               "decode_mha": "fa_fwd_splitkv_decode_b1_h32_nk131072_d128",
+              "decode_mqa": "fa_fwd_gqa_decode_b1_h32_hkv1_nk131072_d128",
               "bwd": "fa_bwd_bf16_n16k_d128_causal_amplified",
               "fp8": "fa_fwd_fp8_bf16_n16k_d128_causal_amplified",
               "gqa": "fa_fwd_gqa_hkv8_bf16_n16k_d128_causal_amplified"}

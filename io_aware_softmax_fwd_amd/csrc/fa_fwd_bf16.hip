@@ -53,6 +53,8 @@
 // heads (short or non-causal heads: decoding with G heads reads K/V once).
 #include <math.h>
 
+#include <algorithm>
+
 #include "fa_device.h"
 #include "fa_internal.h"
 
@@ -477,87 +479,120 @@ __global__ __launch_bounds__(kThreads, (QB == 1 || D == 64) ? 2 : 1) void fwd_bf
 // Merge of the key chunks of every row: LSE = log sum_s exp(LSE_s) and
 // O = sum_s exp(LSE_s - LSE) O_s, the online-softmax merge applied to whole
 // chunks (zzszmyf.github.io notes, sections 5 and 12.1).  One workgroup per
-// row, so the chunks are read in parallel rather than one memory latency
-// after another: the max and the weight sum over chunks are block
-// reductions, then wave w adds chunks w, w+4, ... over all head dims and
-// the four partial sums meet in LDS.  Chunk 0 always holds key 0, so the
-// max is finite.
-constexpr int kMergeThreads = 256;
+// row, sized so that each lane reads about kMergeBatch chunks: a lane reads
+// four head dims of a chunk with one 16-byte load (one wave-wide load covers
+// 256/D chunks) and issues kMergeBatch such loads before it waits, so a row's
+// chunks arrive in one or two memory latencies rather than one after another.
+// Each lane keeps its own running max (the same online rescaling), and the
+// lanes meet at the row max: lane groups through shuffles, waves in LDS.
+// Chunk 0 always holds key 0, so the row max is finite.
+constexpr int kMergeMaxWaves = 16;
+constexpr int kMergeBatch = 8;
 
 __device__ __forceinline__ float wave_max(float x) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) x = fmaxf(x, __shfl_xor(x, off, 64));
   return x;
 }
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
-  return x;
+
+// Waves per merge workgroup for `splits` chunks of D dims.
+template <int D>
+int merge_waves(int splits) {
+  const int64_t lanes = (int64_t)splits * (D / 4);
+  return (int)std::max<int64_t>(1, std::min<int64_t>(kMergeMaxWaves, (lanes + 64 * kMergeBatch - 1) / (64 * kMergeBatch)));
 }
 
 template <int D>
-__global__ __launch_bounds__(kMergeThreads) void merge_kernel(const float* __restrict__ opart,
-                                                              const float* __restrict__ lpart,
-                                                              unsigned short* __restrict__ o,
-                                                              float* __restrict__ lse,
-                                                              int64_t rows, int splits) {
-  constexpr int NW = kMergeThreads / 64, PER = D / 64;   // dims per lane
-  __shared__ float red[NW];
-  __shared__ float part[NW][D];
+__global__ __launch_bounds__(64 * kMergeMaxWaves) void merge_kernel(const float* __restrict__ opart,
+                                                                   const float* __restrict__ lpart,
+                                                                   unsigned short* __restrict__ o,
+                                                                   float* __restrict__ lse,
+                                                                   int64_t rows, int splits) {
+  constexpr int LPS = D / 4;          // lanes per chunk row, four dims each
+  constexpr int SPI = 64 / LPS;       // chunks per wave-wide load
+  __shared__ float red[kMergeMaxWaves];
+  __shared__ float4 part[kMergeMaxWaves][LPS];
   const int64_t row = blockIdx.x;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int nw = blockDim.x >> 6;
+  const int step = nw * SPI;          // chunks per pass of the workgroup
+  const int sub = lane / LPS, c4 = lane % LPS;
 
-  float mx = -INFINITY;
-  for (int sp = tid; sp < splits; sp += kMergeThreads) mx = fmaxf(mx, lpart[(int64_t)sp * rows + row]);
-  mx = wave_max(mx);
-  if (lane == 0) red[wave] = mx;
-  __syncthreads();
-  mx = red[0];
+  float m = -INFINITY, sum = 0.f;
+  float4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int base = wave * SPI + sub; base < splits; base += kMergeBatch * step) {
+    // indices past the last chunk read the last one again, with LSE -inf
+    float ls[kMergeBatch];
+    float4 a[kMergeBatch];
 #pragma unroll
-  for (int w = 1; w < NW; ++w) mx = fmaxf(mx, red[w]);
-  __syncthreads();
-
-  float sum = 0.f;
-  float acc[PER];
+    for (int u = 0; u < kMergeBatch; ++u) {
+      const int64_t sp = min(base + u * step, splits - 1);
+      ls[u] = lpart[sp * rows + row];
+      a[u] = *reinterpret_cast<const float4*>(opart + (sp * rows + row) * D + 4 * c4);
+    }
+    float mb = m;
 #pragma unroll
-  for (int e = 0; e < PER; ++e) acc[e] = 0.f;
-#pragma unroll 4
-  for (int sp = wave; sp < splits; sp += NW) {
-    const float ls = lpart[(int64_t)sp * rows + row];
-    const float w = ls == -INFINITY ? 0.f : expf(ls - mx);
-    sum += w;
-    const float* src = opart + ((int64_t)sp * rows + row) * D + PER * lane;
-    if constexpr (PER == 2) {
-      const float2 a = *reinterpret_cast<const float2*>(src);
-      acc[0] += w * a.x;
-      acc[1] += w * a.y;
-    } else {
-      acc[0] += w * src[0];
+    for (int u = 0; u < kMergeBatch; ++u) {
+      if (base + u * step >= splits) ls[u] = -INFINITY;
+      mb = fmaxf(mb, ls[u]);
+    }
+    const float r = mb == -INFINITY ? 1.f : expf(m - mb);
+    sum *= r;
+    acc.x *= r;
+    acc.y *= r;
+    acc.z *= r;
+    acc.w *= r;
+    m = mb;
+#pragma unroll
+    for (int u = 0; u < kMergeBatch; ++u) {
+      const float w = ls[u] == -INFINITY ? 0.f : expf(ls[u] - m);
+      sum += w;
+      acc.x += w * a[u].x;
+      acc.y += w * a[u].y;
+      acc.z += w * a[u].z;
+      acc.w += w * a[u].w;
     }
   }
-#pragma unroll
-  for (int e = 0; e < PER; ++e) part[wave][PER * lane + e] = acc[e];
-  if (lane == 0) red[wave] = sum;     // every lane of a wave holds the same sum
+  // the row max, then every lane's sums relative to it
+  float M = wave_max(m);
+  if (lane == 0) red[wave] = M;
   __syncthreads();
-  if (wave != 0) return;
+  M = red[0];
+  for (int w = 1; w < nw; ++w) M = fmaxf(M, red[w]);
+  __syncthreads();
+  const float f = m == -INFINITY ? 0.f : expf(m - M);
+  sum *= f;
+  acc.x *= f;
+  acc.y *= f;
+  acc.z *= f;
+  acc.w *= f;
+  // lanes c4, c4 + LPS, ... of a wave hold the same dims of other chunks
+#pragma unroll
+  for (int off = LPS; off < 64; off <<= 1) {
+    acc.x += __shfl_xor(acc.x, off, 64);
+    acc.y += __shfl_xor(acc.y, off, 64);
+    acc.z += __shfl_xor(acc.z, off, 64);
+    acc.w += __shfl_xor(acc.w, off, 64);
+    sum += __shfl_xor(sum, off, 64);
+  }
+  if (sub == 0) part[wave][c4] = acc;
+  if (lane == 0) red[wave] = sum;
+  __syncthreads();
+  if (wave != 0 || lane >= LPS) return;
   float tot = red[0];
-#pragma unroll
-  for (int w = 1; w < NW; ++w) tot += red[w];
+  float4 t = part[0][lane];
+  for (int w = 1; w < nw; ++w) {
+    tot += red[w];
+    const float4 p = part[w][lane];
+    t.x += p.x;
+    t.y += p.y;
+    t.z += p.z;
+    t.w += p.w;
+  }
   const float inv = 1.f / tot;
-  float r[PER];
-#pragma unroll
-  for (int e = 0; e < PER; ++e) {
-    float t = part[0][PER * lane + e];
-#pragma unroll
-    for (int w = 1; w < NW; ++w) t += part[w][PER * lane + e];
-    r[e] = t * inv;
-  }
-  if constexpr (PER == 2) {
-    *reinterpret_cast<unsigned*>(o + row * D + 2 * lane) = pack_bf16x2(r[0], r[1]);
-  } else {
-    o[row * D + lane] = (unsigned short)(pack_bf16x2(r[0], 0.f) & 0xffffu);
-  }
-  if (lane == 0) lse[row] = mx + logf(tot);
+  const u32x2 out = {pack_bf16x2(t.x * inv, t.y * inv), pack_bf16x2(t.z * inv, t.w * inv)};
+  *reinterpret_cast<u32x2*>(o + row * D + 4 * lane) = out;
+  if (lane == 0) lse[row] = M + logf(tot);
 }
 
 // The same merge for many rows: one thread per (row, 8 head dims), each
@@ -650,7 +685,7 @@ hipError_t launch(const GqaProblem& p, hipStream_t stream) {
     hipLaunchKernelGGL((merge_rows_kernel<D>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
                        stream, opart, lpart, static_cast<unsigned short*>(p.o), p.lse, rows, p.splits);
   } else {
-    hipLaunchKernelGGL((merge_kernel<D>), dim3((unsigned)rows), dim3(kMergeThreads), 0, stream, opart,
+    hipLaunchKernelGGL((merge_kernel<D>), dim3((unsigned)rows), dim3(64 * merge_waves<D>(p.splits)), 0, stream, opart,
                        lpart, static_cast<unsigned short*>(p.o), p.lse, rows, p.splits);
   }
   return hipGetLastError();
