@@ -55,6 +55,9 @@ CASES = [
     (1, 2, 2, 130, 130, 128, True, 1),      # one query head per K/V head
     (1, 4, 1, 1, 1, 64, True, 1),
     (1, 4, 4, 3, 70, 128, True, 2),
+    (1, 16, 2, 4, 1500, 128, True, 6),      # 8 heads x 4 positions: 32 rows, causal, one wave's rows
+    (1, 8, 8, 1, 100, 128, True, 5),        # more chunks than key tiles, fewer tiles than waves
+    (2, 32, 4, 1, 777, 64, False, 3),       # chunks of 4 or 5 tiles, ragged key tail
     (1, 64, 16, 2048, 2048, 64, True, 1),   # d = 64, 512 tiles of 256 rows: two blocks per wave
     (2, 64, 8, 1000, 1000, 64, False, 1),   # the same, packed 256-row tiles crossing heads
 ]
