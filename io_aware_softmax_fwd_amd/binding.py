@@ -33,8 +33,10 @@ High level (torch tensors on a ROCm device):
         workspace=None)                                        -> (dq, dk, dv)
     quantize_qk_fp8(x)                                         -> (x8, xs)
     quantize_v_fp8(v)                                          -> (v8t, vs)
-    fwd_fp8(q8, qs, k8, ks, v8t, vs, shape, scale=None,
-            causal=False)                                      -> (o, lse)
+    fwd_fp8(q8, qs, k8, ks, v8t, vs, scale=None, causal=False) -> (o, lse)
+The high-level functions check every tensor they are given (type, device,
+dtype, shape, contiguity) before any launch, so a mismatched buffer raises
+TypeError or ValueError instead of being read or written out of bounds.
 """
 import ctypes
 import math
@@ -67,6 +69,33 @@ class FaError(RuntimeError):
     def __init__(self, status, what):
         super().__init__("%s failed: %s (status %d)" % (what, fa_strerror(status), status))
         self.status = status
+
+
+def _check(name, t, device, dtype=None, shape=None, min_bytes=None):
+    """Raise unless t is a contiguous torch tensor on `device` with the given
+    dtype and shape (or at least min_bytes bytes)."""
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.device != device:
+        raise ValueError("%s must live on %s" % (name, device))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError("%s must be %s" % (name, dtype))
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s" % (name, tuple(shape)))
+    if min_bytes is not None and t.numel() * t.element_size() < min_bytes:
+        raise ValueError("%s must hold at least %d bytes" % (name, min_bytes))
+
+
+def _gpu_device(name, t):
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.device.type != "cuda":
+        raise ValueError("%s must live on the GPU" % name)
+    return t.device
 
 
 def load():
@@ -195,21 +224,14 @@ def fwd(q, k, v, scale=None, causal=False, out=None, lse=None, stream=None):
     current stream) and returns (o, lse); o has q's dtype, lse is fp32 [B,H,N].
     """
     import torch
-    for name, t in (("q", q), ("k", k), ("v", v)):
-        if not isinstance(t, torch.Tensor):
-            raise TypeError("%s must be a torch.Tensor" % name)
-        if t.device.type != "cuda":
-            raise ValueError("%s must live on the GPU" % name)
-        if not t.is_contiguous():
-            raise ValueError("%s must be contiguous" % name)
-        if t.dim() != 4:
-            raise ValueError("%s must be [B, H, N, d]" % name)
+    dev = _gpu_device("q", q)
+    _check("q", q, dev)
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, N, d]")
     if q.dtype not in (torch.bfloat16, torch.float32):
         raise TypeError("q must be bfloat16 or float32")
-    if k.dtype != q.dtype or v.dtype != q.dtype:
-        raise TypeError("q, k, v must share one dtype")
-    if k.shape != q.shape or v.shape != q.shape:
-        raise ValueError("q, k, v must share one shape")
+    for name, t in (("k", k), ("v", v)):
+        _check(name, t, dev, q.dtype, q.shape)
     B, H, N, d = q.shape
     if scale is None:
         scale = 1.0 / math.sqrt(d)
@@ -217,10 +239,8 @@ def fwd(q, k, v, scale=None, causal=False, out=None, lse=None, stream=None):
         out = torch.empty_like(q)
     if lse is None:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
-    if out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
-        raise ValueError("out must be a contiguous tensor like q")
-    if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
-        raise ValueError("lse must be a contiguous float32 [B, H, N] tensor")
+    _check("out", out, dev, q.dtype, q.shape)
+    _check("lse", lse, dev, torch.float32, (B, H, N))
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream
     f = fa_fwd if q.dtype == torch.bfloat16 else fa_fwd_f32
@@ -238,17 +258,17 @@ def fwd_splitkv(q, k, v, scale=None, causal=False, num_splits=None, workspace=No
     library's suggestion for this GPU; workspace (a uint8 device tensor) is
     allocated here if not given.  Returns (o, lse)."""
     import torch
-    for name, t in (("q", q), ("k", k), ("v", v)):
-        if not isinstance(t, torch.Tensor):
-            raise TypeError("%s must be a torch.Tensor" % name)
-        if t.device.type != "cuda" or not t.is_contiguous() or t.dim() != 4:
-            raise ValueError("%s must be a contiguous 4-D GPU tensor" % name)
-        if t.dtype != torch.bfloat16:
-            raise TypeError("%s must be bfloat16" % name)
+    dev = _gpu_device("q", q)
+    _check("q", q, dev, torch.bfloat16)
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, Nq, d]")
     B, H, Nq, d = q.shape
+    _gpu_device("k", k)
+    if k.dim() != 4:
+        raise ValueError("k must be [B, H, Nk, d]")
     Nk = k.shape[2]
-    if k.shape != (B, H, Nk, d) or v.shape != k.shape:
-        raise ValueError("k and v must be [B, H, Nk, d] with q's B, H and d")
+    for name, t in (("k", k), ("v", v)):
+        _check(name, t, dev, torch.bfloat16, (B, H, Nk, d))
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if num_splits is None:
@@ -257,10 +277,13 @@ def fwd_splitkv(q, k, v, scale=None, causal=False, num_splits=None, workspace=No
     need = fa_fwd_splitkv_workspace_size(B, H, Nq, d, num_splits)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _check("workspace", workspace, dev)
     if out is None:
         out = torch.empty_like(q)
     if lse is None:
         lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    _check("out", out, dev, torch.bfloat16, q.shape)
+    _check("lse", lse, dev, torch.float32, (B, H, Nq))
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream
     st = fa_fwd_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
@@ -279,17 +302,17 @@ def fwd_gqa(q, k, v, scale=None, causal=False, num_splits=1, workspace=None,
     than one split a workspace (uint8 device tensor) is allocated here if not
     given.  Returns (o, lse)."""
     import torch
-    for name, t in (("q", q), ("k", k), ("v", v)):
-        if not isinstance(t, torch.Tensor):
-            raise TypeError("%s must be a torch.Tensor" % name)
-        if t.device.type != "cuda" or not t.is_contiguous() or t.dim() != 4:
-            raise ValueError("%s must be a contiguous 4-D GPU tensor" % name)
-        if t.dtype != torch.bfloat16:
-            raise TypeError("%s must be bfloat16" % name)
+    dev = _gpu_device("q", q)
+    _check("q", q, dev, torch.bfloat16)
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, Nq, d]")
     B, H, Nq, d = q.shape
+    _gpu_device("k", k)
+    if k.dim() != 4:
+        raise ValueError("k must be [B, Hkv, Nk, d]")
     Hkv, Nk = k.shape[1], k.shape[2]
-    if k.shape != (B, Hkv, Nk, d) or v.shape != k.shape:
-        raise ValueError("k and v must be [B, Hkv, Nk, d] with q's B and d")
+    for name, t in (("k", k), ("v", v)):
+        _check(name, t, dev, torch.bfloat16, (B, Hkv, Nk, d))
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if num_splits is None:
@@ -300,11 +323,14 @@ def fwd_gqa(q, k, v, scale=None, causal=False, num_splits=1, workspace=None,
         if workspace is None:
             need = fa_fwd_splitkv_workspace_size(B, H, Nq, d, num_splits)
             workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+        _check("workspace", workspace, dev)
         ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
     if out is None:
         out = torch.empty_like(q)
     if lse is None:
         lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    _check("out", out, dev, torch.bfloat16, q.shape)
+    _check("lse", lse, dev, torch.float32, (B, H, Nq))
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream
     st = fa_fwd_gqa(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
@@ -321,23 +347,20 @@ def bwd(q, k, v, o, lse, dout, scale=None, causal=False, workspace=None, stream=
     (dq, dk, dv) as bf16 tensors; the workspace (uint8 device tensor) is
     allocated here if not given."""
     import torch
-    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
-        if not isinstance(t, torch.Tensor):
-            raise TypeError("%s must be a torch.Tensor" % name)
-        if t.device.type != "cuda" or not t.is_contiguous() or t.dim() != 4:
-            raise ValueError("%s must be a contiguous 4-D GPU tensor" % name)
-        if t.dtype != torch.bfloat16:
-            raise TypeError("%s must be bfloat16" % name)
-        if t.shape != q.shape:
-            raise ValueError("%s must have q's shape" % name)
+    dev = _gpu_device("q", q)
+    _check("q", q, dev, torch.bfloat16)
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, N, d]")
+    for name, t in (("k", k), ("v", v), ("o", o), ("dout", dout)):
+        _check(name, t, dev, torch.bfloat16, q.shape)
     B, H, N, d = q.shape
-    if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
-        raise ValueError("lse must be a contiguous float32 [B, H, N] tensor")
+    _check("lse", lse, dev, torch.float32, (B, H, N))
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if workspace is None:
         workspace = torch.empty(max(1, fa_bwd_workspace_size(B, H, N, d)), dtype=torch.uint8,
                                 device=q.device)
+    _check("workspace", workspace, dev)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream
@@ -352,10 +375,9 @@ def bwd(q, k, v, o, lse, dout, scale=None, causal=False, workspace=None, stream=
 
 def _bf16_4d(name, t):
     import torch
-    if not isinstance(t, torch.Tensor):
-        raise TypeError("%s must be a torch.Tensor" % name)
-    if t.device.type != "cuda" or not t.is_contiguous() or t.dim() != 4 or t.dtype != torch.bfloat16:
-        raise ValueError("%s must be a contiguous 4-D bf16 GPU tensor" % name)
+    _check(name, t, _gpu_device(name, t), torch.bfloat16)
+    if t.dim() != 4:
+        raise ValueError("%s must be [B, H, N, d]" % name)
 
 
 def quantize_qk_fp8(x, stream=None):
@@ -396,7 +418,18 @@ def fwd_fp8(q8, qs, k8, ks, v8t, vs, scale=None, causal=False, stream=None):
     quantize_qk_fp8 and quantize_v_fp8); q8 gives the [B,H,N,d] shape.
     Returns (o bf16 [B,H,N,d], lse fp32 [B,H,N])."""
     import torch
+    dev = _gpu_device("q8", q8)
+    _check("q8", q8, dev, torch.uint8)
+    if q8.dim() != 4:
+        raise ValueError("q8 must be [B, H, N, d]")
     B, H, N, d = q8.shape
+    if d not in (64, 128):
+        raise ValueError("head dimension must be 64 or 128")
+    _check("k8", k8, dev, torch.uint8, (B, H, N, d))
+    for name, t in (("qs", qs), ("ks", ks)):
+        _check(name, t, dev, torch.uint8, (B, H, N, d // 32))
+    _check("v8t", v8t, dev, torch.uint8, min_bytes=fa_fp8_v_bytes(B * H, N, d))
+    _check("vs", vs, dev, torch.uint8, min_bytes=fa_fp8_v_scale_bytes(B * H, N, d))
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     o = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=q8.device)

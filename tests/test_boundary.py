@@ -276,3 +276,25 @@ def test_fwd_fp8_bad_arguments(kw, status):
     a.update(kw)
     assert fa.fa_fwd_fp8(a["q8"], a["qs"], a["k8"], a["ks"], a["v8t"], a["vs"], a["o"], a["lse"], a["B"],
                          a["H"], a["N"], a["d"], a["scale"], a["causal"], a["stream"]) == status
+
+
+def test_binding_tensor_checks_on_host():
+    """The binding's tensor check (used by every high-level function before a
+    launch) on CPU tensors: type, device, contiguity, dtype, shape, size."""
+    import torch
+    from io_aware_softmax_fwd_amd.binding import _check
+    cpu = torch.device("cpu")
+    t = torch.zeros((2, 3, 4, 64), dtype=torch.bfloat16)
+    _check("t", t, cpu, torch.bfloat16, (2, 3, 4, 64), min_bytes=t.numel() * 2)
+    with pytest.raises(TypeError):
+        _check("t", [1, 2], cpu)
+    with pytest.raises(ValueError, match="live on"):
+        _check("t", t, torch.device("cuda", 0))
+    with pytest.raises(ValueError, match="contiguous"):
+        _check("t", t.transpose(2, 3), cpu)
+    with pytest.raises(TypeError, match="bfloat16"):
+        _check("t", t.float(), cpu, torch.bfloat16)
+    with pytest.raises(ValueError, match="shape"):
+        _check("t", t, cpu, torch.bfloat16, (2, 3, 5, 64))
+    with pytest.raises(ValueError, match="bytes"):
+        _check("t", t, cpu, min_bytes=t.numel() * 2 + 1)
