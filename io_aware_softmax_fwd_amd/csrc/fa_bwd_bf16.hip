@@ -346,7 +346,7 @@ struct BwdKV {
     const float* lt = lbuf[PAR];
     const float* dt = dbuf[PAR];
     // The two 32-query halves run as a loop, not unrolled: two copies in
-    // flight need more registers than one wave per SIMD has.  Halves wholly
+    // flight need more registers than a wave has.  Halves wholly
     // above the diagonal are still computed (their probabilities are 0);
     // skipping them made the accumulators pass through a branch merge that
     // the compiler could only serve by spilling.
@@ -424,7 +424,11 @@ struct BwdKV {
 };
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
+// Two workgroups per CU (2 x 77 KB of LDS at d = 128): 256 registers a
+// lane.  The causal variants then keep some values in scratch, but only in
+// the loop over the diagonal query tiles, which are a few of each
+// workgroup's tiles; the loop over the unmasked tiles stays in registers.
+__global__ __launch_bounds__(kBwdThreads, 2) void bwd_dkdv_kernel(
     const unsigned short* __restrict__ q, const unsigned short* __restrict__ k,
     const unsigned short* __restrict__ v, const unsigned short* __restrict__ dout,
     const float* __restrict__ lse, const float* __restrict__ dws, unsigned short* __restrict__ dk,
