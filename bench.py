@@ -309,7 +309,8 @@ def decode_bench(fa, args):
 
 
 def bwd_bench(fa, args, w, x):
-    """Time fa_bwd on the workload; returns the JSON line."""
+    """Time fa_bwd on the workload (fa_bwd_gqa with --hkv: K and V keep the
+    workload's first HKV heads); returns the JSON line."""
     import torch
     dev = torch.device("cuda:0")
 
@@ -320,19 +321,23 @@ def bwd_bench(fa, args, w, x):
 
     rng = np.random.default_rng(1000 * w.cfg + 6)
     g = rng.standard_normal((w.B, w.H, w.N, w.d), dtype=np.float32)
+    hkv = args.hkv or w.H
     q, k, v = up(x["q_bits"]), up(x["k_bits"]), up(x["v_bits"])
+    k, v = k[:, :hkv].contiguous(), v[:, :hkv].contiguous()
     dO = up(W.bf16_bits_rne(g))
-    o, lse = fa.fwd(q, k, v, scale=w.scale, causal=w.causal)
-    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
-    ws = torch.empty(fa.fa_bwd_workspace_size(w.B, w.H, w.N, w.d), dtype=torch.uint8, device=dev)
+    o, lse = fa.fwd_gqa(q, k, v, scale=w.scale, causal=w.causal)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(fa.fa_bwd_gqa_workspace_size(w.B, w.H, hkv, w.N, w.d), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
-    a = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dO.data_ptr(), lse.data_ptr(),
-         dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), w.B, w.H, w.N, w.d, w.scale, int(w.causal),
-         ws.data_ptr(), ws.numel(), stream.cuda_stream)
+    heads = (w.B, w.H, hkv) if args.hkv else (w.B, w.H)
+    a = ((q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dO.data_ptr(), lse.data_ptr(),
+          dq.data_ptr(), dk.data_ptr(), dv.data_ptr()) + heads +
+         (w.N, w.d, w.scale, int(w.causal), ws.data_ptr(), ws.numel(), stream.cuda_stream))
+    call = fa.fa_bwd_gqa if args.hkv else fa.fa_bwd
     for _ in range(args.warmup):
-        st = fa.fa_bwd(*a)
+        st = call(*a)
         if st != 0:
-            raise fa.FaError(st, "fa_bwd")
+            raise fa.FaError(st, call.__name__)
     torch.cuda.synchronize()
     for t in (dq, dk, dv):
         if not torch.isfinite(t.float()).all():
@@ -341,7 +346,7 @@ def bwd_bench(fa, args, w, x):
     t0 = time.perf_counter()
     ev0.record(stream)
     for _ in range(args.steps):
-        fa.fa_bwd(*a)
+        call(*a)
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -352,8 +357,9 @@ def bwd_bench(fa, args, w, x):
             "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall * 1e3 / args.steps, 4),
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
             "data": "synthetic (seeded N(0,1) draws, bf16-rounded)",
-            "config": {"workload": w.name + "_bwd", "B": w.B, "H": w.H, "N": w.N, "d": w.d,
-                       "causal": w.causal, "flops": flops, "entry_point": "fa_bwd"},
+            "config": {"workload": w.name + "_bwd" + ("_hkv%d" % hkv if args.hkv else ""), "B": w.B,
+                       "H": w.H, "Hkv": hkv, "N": w.N, "d": w.d, "causal": w.causal, "flops": flops,
+                       "entry_point": "fa_bwd_gqa" if args.hkv else "fa_bwd"},
             "roofline": {"bound": "mfma", "achieved": round(flops / (ms * 1e-3) / 1e12, 2),
                          "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),

@@ -189,6 +189,30 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
 size_t fa_bwd_workspace_size(int B, int H, int N, int d);
 
 /*
+ * Backward pass with grouped K/V heads (MQA/GQA, as fa_fwd_gqa with
+ * Nq = Nk = N): q, o, dout, dq are [B,H,N,d] bf16, lse [B,H,N] fp32, and
+ * k, v, dk, dv are [B,Hkv,N,d] bf16, query head h of batch b reading K/V head
+ * h / (H / Hkv) of batch b.  Since a shared K/V head enters the forward once
+ * per query head of its group, its gradient is the sum of the per-head
+ * gradients (the chain rule through the copies): each query head's fp32
+ * dK and dV go to the workspace and a third kernel sums every group in head
+ * order and rounds to bf16, so results stay reproducible bit for bit.
+ *   workspace : at least fa_bwd_gqa_workspace_size(B, H, Hkv, N, d) bytes,
+ *               16-byte aligned; Hkv == H needs only fa_bwd's workspace and
+ *               gives exactly fa_bwd's results.
+ * Other arguments and errors as for fa_bwd, plus FA_ERR_HEADS when Hkv does
+ * not divide H.
+ */
+int fa_bwd_gqa(const void* q, const void* k, const void* v, const void* o, const void* dout,
+               const float* lse, void* dq, void* dk, void* dv, int B, int H, int Hkv, int N, int d,
+               float scale, int causal, void* workspace, size_t workspace_bytes,
+               hipStream_t stream);
+
+/* Bytes of workspace fa_bwd_gqa needs (0 if an argument is out of range).
+ * Host only, no HIP call. */
+size_t fa_bwd_gqa_workspace_size(int B, int H, int Hkv, int N, int d);
+
+/*
  * fp8 forward with per-block scales: the low-precision variant of the method
  * (zzszmyf.github.io notes "FlashAttention 原理是什么", section 10 item ③ and
  * section 12.2: block-wise quantization with one scale per block).  Inputs

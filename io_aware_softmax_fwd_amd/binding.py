@@ -17,6 +17,9 @@ Low level (same names and arguments as the C functions, raw pointers):
     fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, scale, causal,
            workspace, workspace_bytes, stream)                 -> status
     fa_bwd_workspace_size(B, H, N, d)                          -> bytes
+    fa_bwd_gqa(q, k, v, o, dout, lse, dq, dk, dv, B, H, Hkv, N, d, scale,
+               causal, workspace, workspace_bytes, stream)     -> status
+    fa_bwd_gqa_workspace_size(B, H, Hkv, N, d)                 -> bytes
     fa_quantize_qk_fp8(x, rows, d, x8, xs, stream)             -> status
     fa_quantize_v_fp8(v, BH, N, d, v8t, vs, stream)            -> status
     fa_fp8_v_bytes(BH, N, d), fa_fp8_v_scale_bytes(BH, N, d)   -> bytes
@@ -31,6 +34,8 @@ High level (torch tensors on a ROCm device):
             workspace=None)                                    -> (o, lse)
     bwd(q, k, v, o, lse, dout, scale=None, causal=False,
         workspace=None)                                        -> (dq, dk, dv)
+    bwd_gqa(q, k, v, o, lse, dout, scale=None, causal=False,
+            workspace=None)                                    -> (dq, dk, dv)
     quantize_qk_fp8(x)                                         -> (x8, xs)
     quantize_v_fp8(v)                                          -> (v8t, vs)
     fwd_fp8(q8, qs, k8, ks, v8t, vs, scale=None, causal=False) -> (o, lse)
@@ -59,7 +64,7 @@ FA_ERR_HEADS = 11
 
 EXPORTED = ("fa_fwd", "fa_fwd_f32", "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_size",
             "fa_fwd_splitkv_num_splits", "fa_fwd_gqa", "fa_fwd_gqa_num_splits", "fa_bwd",
-            "fa_bwd_workspace_size", "fa_quantize_qk_fp8", "fa_quantize_v_fp8", "fa_fp8_v_bytes",
+            "fa_bwd_workspace_size", "fa_bwd_gqa", "fa_bwd_gqa_workspace_size", "fa_quantize_qk_fp8", "fa_quantize_v_fp8", "fa_fp8_v_bytes",
             "fa_fp8_v_scale_bytes", "fa_fwd_fp8", "fa_strerror")
 
 _lib = None
@@ -133,6 +138,12 @@ def load():
                             ctypes.c_void_p])
     lib.fa_bwd_workspace_size.restype = ctypes.c_size_t
     lib.fa_bwd_workspace_size.argtypes = [ctypes.c_int] * 4
+    lib.fa_bwd_gqa.restype = ctypes.c_int
+    lib.fa_bwd_gqa.argtypes = ([ctypes.c_void_p] * 9 + [ctypes.c_int] * 5 +
+                               [ctypes.c_float, ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t,
+                                ctypes.c_void_p])
+    lib.fa_bwd_gqa_workspace_size.restype = ctypes.c_size_t
+    lib.fa_bwd_gqa_workspace_size.argtypes = [ctypes.c_int] * 5
     lib.fa_quantize_qk_fp8.restype = ctypes.c_int
     lib.fa_quantize_qk_fp8.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p,
                                        ctypes.c_void_p, ctypes.c_void_p]
@@ -192,6 +203,16 @@ def fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, scale, causal, workspa
 
 def fa_bwd_workspace_size(B, H, N, d):
     return int(load().fa_bwd_workspace_size(B, H, N, d))
+
+
+def fa_bwd_gqa(q, k, v, o, dout, lse, dq, dk, dv, B, H, Hkv, N, d, scale, causal, workspace,
+               workspace_bytes, stream):
+    return load().fa_bwd_gqa(q, k, v, o, dout, lse, dq, dk, dv, B, H, Hkv, N, d, scale, causal,
+                             workspace, workspace_bytes, stream)
+
+
+def fa_bwd_gqa_workspace_size(B, H, Hkv, N, d):
+    return int(load().fa_bwd_gqa_workspace_size(B, H, Hkv, N, d))
 
 
 def fa_quantize_qk_fp8(x, rows, d, x8, xs, stream):
@@ -370,6 +391,45 @@ def bwd(q, k, v, o, lse, dout, scale=None, causal=False, workspace=None, stream=
                 workspace.numel() * workspace.element_size(), stream)
     if st != FA_OK:
         raise FaError(st, "fa_bwd")
+    return dq, dk, dv
+
+
+def bwd_gqa(q, k, v, o, lse, dout, scale=None, causal=False, workspace=None, stream=None):
+    """Backward pass with grouped K/V heads: q, o, dout [B,H,N,d] and k, v
+    [B,Hkv,N,d] bf16 (Hkv dividing H), lse [B,H,N] fp32 from the forward, all
+    contiguous on the GPU.  Returns (dq [B,H,N,d], dk and dv [B,Hkv,N,d]) as
+    bf16; the workspace (uint8 device tensor) is allocated here if not given."""
+    import torch
+    dev = _gpu_device("q", q)
+    _check("q", q, dev, torch.bfloat16)
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, N, d]")
+    B, H, N, d = q.shape
+    for name, t in (("o", o), ("dout", dout)):
+        _check(name, t, dev, torch.bfloat16, q.shape)
+    _gpu_device("k", k)
+    if k.dim() != 4:
+        raise ValueError("k must be [B, Hkv, N, d]")
+    Hkv = k.shape[1]
+    for name, t in (("k", k), ("v", v)):
+        _check(name, t, dev, torch.bfloat16, (B, Hkv, N, d))
+    _check("lse", lse, dev, torch.float32, (B, H, N))
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if workspace is None:
+        workspace = torch.empty(max(1, fa_bwd_gqa_workspace_size(B, H, Hkv, N, d)), dtype=torch.uint8,
+                                device=q.device)
+    _check("workspace", workspace, dev)
+    dq = torch.empty_like(q)
+    dk, dv = torch.empty_like(k), torch.empty_like(v)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    st = fa_bwd_gqa(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
+                    lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, Hkv, N, d,
+                    float(scale), int(bool(causal)), workspace.data_ptr(),
+                    workspace.numel() * workspace.element_size(), stream)
+    if st != FA_OK:
+        raise FaError(st, "fa_bwd_gqa")
     return dq, dk, dv
 
 

@@ -129,10 +129,11 @@ int choose_splits(int B, int H, int Hkv, int Nq, int Nk, int causal, int num_cus
 }
 
 int validate_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
-                 const float* lse, const void* dq, const void* dk, const void* dv, int B, int H, int N,
-                 int d, float scale, int causal, const void* ws, size_t ws_bytes) {
+                 const float* lse, const void* dq, const void* dk, const void* dv, int B, int H,
+                 int Hkv, int N, int d, float scale, int causal, const void* ws, size_t ws_bytes) {
   if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return FA_ERR_NULL;
-  if (B < 1 || H < 1 || N < 1) return FA_ERR_SHAPE;
+  if (B < 1 || H < 1 || Hkv < 1 || N < 1) return FA_ERR_SHAPE;
+  if (H % Hkv != 0) return FA_ERR_HEADS;
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED_D;
   const int64_t rows = (int64_t)B * H * N;
   if (rows * d >= kMaxElems || grid_too_large((int64_t)B * H, N)) return FA_ERR_SHAPE;
@@ -142,12 +143,12 @@ int validate_bwd(const void* q, const void* k, const void* v, const void* o, con
   const void* all[] = {q, k, v, o, dout, lse, dq, dk, dv, ws};
   for (const void* p : all)
     if (p && misaligned(p)) return FA_ERR_ALIGN;
-  const int64_t wb = fa::bwd_workspace_bytes(B, H, N);
+  const int64_t wb = fa::bwd_layout(B, H, Hkv, N, d).total;
   if (!ws || (int64_t)ws_bytes < wb) return FA_ERR_WORKSPACE;
   // outputs (dq, dk, dv, workspace) overlap nothing else
-  const int64_t tb = rows * d * 2, lb = rows * 4;
+  const int64_t tb = rows * d * 2, kb = (int64_t)B * Hkv * N * d * 2, lb = rows * 4;
   const void* ptr[] = {q, k, v, o, dout, lse, dq, dk, dv, ws};
-  const int64_t len[] = {tb, tb, tb, tb, tb, lb, tb, tb, tb, wb};
+  const int64_t len[] = {tb, kb, kb, tb, tb, lb, tb, kb, kb, wb};
   for (int a = 6; a < 10; ++a)
     for (int b = 0; b < 10; ++b)
       if (a != b && overlap(ptr[a], len[a], ptr[b], len[b])) return FA_ERR_ALIAS;
@@ -229,17 +230,30 @@ int fa_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse,
 
 size_t fa_bwd_workspace_size(int B, int H, int N, int d) {
   if (B < 1 || H < 1 || N < 1 || (d != 64 && d != 128)) return 0;
-  return (size_t)fa::bwd_workspace_bytes(B, H, N);
+  return (size_t)fa::bwd_layout(B, H, H, N, d).total;
+}
+
+size_t fa_bwd_gqa_workspace_size(int B, int H, int Hkv, int N, int d) {
+  if (B < 1 || H < 1 || Hkv < 1 || H % Hkv != 0 || N < 1 || (d != 64 && d != 128)) return 0;
+  if ((int64_t)B * H * N * d >= kMaxElems) return 0;
+  return (size_t)fa::bwd_layout(B, H, Hkv, N, d).total;
+}
+
+int fa_bwd_gqa(const void* q, const void* k, const void* v, const void* o, const void* dout,
+               const float* lse, void* dq, void* dk, void* dv, int B, int H, int Hkv, int N, int d,
+               float scale, int causal, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  const int st = validate_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, H, Hkv, N, d, scale, causal,
+                              workspace, workspace_bytes);
+  if (st != FA_OK) return st;
+  const fa::BwdProblem p{q, k, v, o, dout, lse, dq, dk, dv, B, H, Hkv, N, d, scale, causal, workspace};
+  return fa::launch_bwd_bf16(p, stream) == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
            const float* lse, void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale,
            int causal, void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  const int st = validate_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, scale, causal,
-                              workspace, workspace_bytes);
-  if (st != FA_OK) return st;
-  const fa::BwdProblem p{q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, scale, causal, workspace};
-  return fa::launch_bwd_bf16(p, stream) == hipSuccess ? FA_OK : FA_ERR_HIP;
+  return fa_bwd_gqa(q, k, v, o, dout, lse, dq, dk, dv, B, H, H, N, d, scale, causal, workspace,
+                    workspace_bytes, stream);
 }
 
 int fa_quantize_qk_fp8(const void* x, int64_t rows, int d, void* x8, void* xs, hipStream_t stream) {

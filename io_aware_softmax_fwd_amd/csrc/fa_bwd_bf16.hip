@@ -123,6 +123,23 @@ __device__ __forceinline__ void store_rowT(unsigned short* row, const f32x16 (&a
     }
 }
 
+// The same rows as fp32 (partial sums of a group of query heads).
+template <int D>
+__device__ __forceinline__ void store_rowT_f32(float* row, const f32x16 (&acc)[D / 32], float mul, int hl) {
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int dim = 32 * db + 8 * g + 4 * hl;
+      const float4 w = {acc[db][4 * g] * mul, acc[db][4 * g + 1] * mul, acc[db][4 * g + 2] * mul,
+                        acc[db][4 * g + 3] * mul};
+      *reinterpret_cast<float4*>(row + dim) = w;
+    }
+}
+
+// K/V head read by query head bh (of B*H) when G query heads share one.
+__device__ __forceinline__ int kv_head(int bh, int H, int G) { return (bh / H) * (H / G) + (bh % H) / G; }
+
 // ----------------------------------------------------------------- dQ kernel
 template <int D, bool CAUSAL>
 struct BwdQ {
@@ -213,7 +230,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(
     const unsigned short* __restrict__ v, const unsigned short* __restrict__ o,
     const unsigned short* __restrict__ dout, const float* __restrict__ lse,
     unsigned short* __restrict__ dq, float* __restrict__ dws, int N, int BH, int n_qtiles,
-    float scale, int hg) {
+    float scale, int hg, int H, int G) {
   using F = BwdQ<D, CAUSAL>;
   __shared__ __attribute__((aligned(1024))) unsigned char k_lds0[Dma<D, F::KSTR>::bytes];
   __shared__ __attribute__((aligned(1024))) unsigned char k_lds1[Dma<D, F::KSTR>::bytes];
@@ -227,14 +244,15 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(
   const int qt = n_qtiles - 1 - rank;   // heaviest causal tiles first
   const int q0 = qt * BR;
   const int64_t head = (int64_t)bh * N * D;
+  const int64_t kvh = (int64_t)kv_head(bh, H, G) * N * D;
 
   F f;
   f.kbuf[0] = k_lds0;
   f.kbuf[1] = k_lds1;
   f.vbuf[0] = v_lds0;
   f.vbuf[1] = v_lds1;
-  f.kh = k + head;
-  f.vh = v + head;
+  f.kh = k + kvh;
+  f.vh = v + kvh;
   f.N = N;
   f.wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   f.l32 = lane & 31;
@@ -432,7 +450,8 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dkdv_kernel(
     const unsigned short* __restrict__ q, const unsigned short* __restrict__ k,
     const unsigned short* __restrict__ v, const unsigned short* __restrict__ dout,
     const float* __restrict__ lse, const float* __restrict__ dws, unsigned short* __restrict__ dk,
-    unsigned short* __restrict__ dv, int N, int BH, float scale, int hg) {
+    unsigned short* __restrict__ dv, int N, int BH, float scale, int hg, int H, int G,
+    float* __restrict__ pdk, float* __restrict__ pdv) {
   using F = BwdKV<D, CAUSAL>;
   __shared__ __attribute__((aligned(1024))) unsigned char q_lds0[Dma<D, F::STR>::bytes];
   __shared__ __attribute__((aligned(1024))) unsigned char q_lds1[Dma<D, F::STR>::bytes];
@@ -449,6 +468,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dkdv_kernel(
   xcd_order(blockIdx.x, BH, (N + BK - 1) / BK, hg, bh, kt);
   const int k0 = kt * BK;
   const int64_t head = (int64_t)bh * N * D;
+  const int64_t kvh = (int64_t)kv_head(bh, H, G) * N * D;
 
   F f;
   f.qbuf[0] = q_lds0;
@@ -471,8 +491,8 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dkdv_kernel(
   f.kj = k0 + 32 * f.wave + f.l32;
   f.c = scale * kLog2e;
   const bool valid = f.kj < N;
-  load_row_fragments<D>(k + head + (int64_t)f.kj * D, valid, f.hl, f.kf);
-  load_row_fragments<D>(v + head + (int64_t)f.kj * D, valid, f.hl, f.vf);
+  load_row_fragments<D>(k + kvh + (int64_t)f.kj * D, valid, f.hl, f.kf);
+  load_row_fragments<D>(v + kvh + (int64_t)f.kj * D, valid, f.hl, f.vf);
 #pragma unroll
   for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -513,14 +533,52 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dkdv_kernel(
     }
   }
   if (valid) {
-    store_rowT<D>(dk + head + (int64_t)f.kj * D, f.dk, scale, f.hl);
-    store_rowT<D>(dv + head + (int64_t)f.kj * D, f.dv, 1.f, f.hl);
+    if (G == 1) {
+      store_rowT<D>(dk + head + (int64_t)f.kj * D, f.dk, scale, f.hl);
+      store_rowT<D>(dv + head + (int64_t)f.kj * D, f.dv, 1.f, f.hl);
+    } else {
+      // this query head's share; the group's shares are summed afterwards
+      store_rowT_f32<D>(pdk + head + (int64_t)f.kj * D, f.dk, scale, f.hl);
+      store_rowT_f32<D>(pdv + head + (int64_t)f.kj * D, f.dv, 1.f, f.hl);
+    }
+  }
+}
+
+// dK and dV of each K/V head: the sum of its G query heads' fp32 shares, in
+// head order (a fixed order, so the result is reproducible), rounded to
+// bf16.  One thread per (K/V head row, 8 head dims).
+template <int D>
+__global__ __launch_bounds__(256) void bwd_group_sum_kernel(const float* __restrict__ pdk,
+                                                            const float* __restrict__ pdv,
+                                                            unsigned short* __restrict__ dk,
+                                                            unsigned short* __restrict__ dv,
+                                                            int64_t kv_rows, int N, int G) {
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t row = t / (D / 8);            // row of [B*Hkv*N]
+  const int c8 = (int)(t % (D / 8));
+  if (row >= kv_rows) return;
+  const int64_t bkv = row / N, n = row % N;
+  const int64_t first = (bkv * G * N + n) * D + 8 * c8;   // query head bkv*G, same row
+#pragma unroll
+  for (int which = 0; which < 2; ++which) {
+    const float* src = (which ? pdv : pdk) + first;
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int g = 0; g < G; ++g) {
+      const float4 a = *reinterpret_cast<const float4*>(src + (int64_t)g * N * D);
+      const float4 b = *reinterpret_cast<const float4*>(src + (int64_t)g * N * D + 4);
+      acc[0] += a.x; acc[1] += a.y; acc[2] += a.z; acc[3] += a.w;
+      acc[4] += b.x; acc[5] += b.y; acc[6] += b.z; acc[7] += b.w;
+    }
+    const u32x4 out = {pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
+                       pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7])};
+    *reinterpret_cast<u32x4*>((which ? dv : dk) + row * D + 8 * c8) = out;
   }
 }
 
 template <int D, bool CAUSAL>
 hipError_t launch_bwd(const BwdProblem& p, hipStream_t stream) {
   const int BH = p.B * p.H;
+  const int G = p.H / p.Hkv;
   const int n_qtiles = (p.N + 32 * kBwdWaves - 1) / (32 * kBwdWaves);
   const int hg = xcd_head_group(BH, n_qtiles, 1, CAUSAL ? n_qtiles : 0, 1);
   const unsigned short* q = static_cast<const unsigned short*>(p.q);
@@ -531,13 +589,24 @@ hipError_t launch_bwd(const BwdProblem& p, hipStream_t stream) {
   hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)((int64_t)n_qtiles * BH)),
                      dim3(kBwdThreads), 0, stream, q, k, v,
                      static_cast<const unsigned short*>(p.o), dout, p.lse,
-                     static_cast<unsigned short*>(p.dq), dws, p.N, BH, n_qtiles, p.scale, hg);
+                     static_cast<unsigned short*>(p.dq), dws, p.N, BH, n_qtiles, p.scale, hg, p.H, G);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  const BwdLayout L = bwd_layout(p.B, p.H, p.Hkv, p.N, D);
+  unsigned char* ws = static_cast<unsigned char*>(p.workspace);
+  float* pdk = G > 1 ? reinterpret_cast<float*>(ws + L.dk_offset) : nullptr;
+  float* pdv = G > 1 ? reinterpret_cast<float*>(ws + L.dv_offset) : nullptr;
   hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)((int64_t)n_qtiles * BH)),
                      dim3(kBwdThreads), 0, stream, q, k, v, dout, p.lse, dws,
                      static_cast<unsigned short*>(p.dk), static_cast<unsigned short*>(p.dv), p.N, BH,
-                     p.scale, hg);
+                     p.scale, hg, p.H, G, pdk, pdv);
+  e = hipGetLastError();
+  if (e != hipSuccess || G == 1) return e;
+  const int64_t kv_rows = (int64_t)p.B * p.Hkv * p.N;
+  const int64_t threads = kv_rows * (D / 8);
+  hipLaunchKernelGGL((bwd_group_sum_kernel<D>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
+                     stream, pdk, pdv, static_cast<unsigned short*>(p.dk), static_cast<unsigned short*>(p.dv),
+                     kv_rows, p.N, G);
   return hipGetLastError();
 }
 

@@ -35,9 +35,12 @@ struct GqaProblem {
   void* workspace;
 };
 
-// Backward problem (square, bf16): gradients dq, dk, dv of O = softmax(scale
-// Q K^T) V for the upstream gradient dout, from the forward's o and lse;
-// `workspace` holds the per-row D = <dO, O> (fp32 [B*H*N]).
+// Backward problem (bf16, Nq = Nk = N): gradients dq, dk, dv of O =
+// softmax(scale Q K^T) V for the upstream gradient dout, from the forward's
+// o and lse.  q, o, dout, dq are [B,H,N,d]; k, v, dk, dv are [B,Hkv,N,d],
+// query head h reading K/V head h / (H/Hkv).  `workspace` holds the per-row
+// D = <dO, O> (fp32 [B*H*N]) and, when Hkv < H, the per-query-head fp32
+// partial dK and dV ([B*H, N, d] each) that are summed over each group.
 struct BwdProblem {
   const void* q;
   const void* k;
@@ -48,15 +51,25 @@ struct BwdProblem {
   void* dq;
   void* dk;
   void* dv;
-  int B, H, N, d;
+  int B, H, Hkv, N, d;
   float scale;
   int causal;
   void* workspace;
 };
 
-inline int64_t bwd_workspace_bytes(int B, int H, int N) {
-  return ((int64_t)B * H * N * 4 + 255) / 256 * 256;
+struct BwdLayout {
+  int64_t d_bytes, dk_offset, dv_offset, total;
+};
+inline BwdLayout bwd_layout(int B, int H, int Hkv, int N, int d) {
+  BwdLayout L;
+  L.d_bytes = ((int64_t)B * H * N * 4 + 255) / 256 * 256;
+  const int64_t part = Hkv < H ? ((int64_t)B * H * N * d * 4 + 255) / 256 * 256 : 0;
+  L.dk_offset = L.d_bytes;
+  L.dv_offset = L.d_bytes + part;
+  L.total = L.d_bytes + 2 * part;
+  return L;
 }
+inline int64_t bwd_workspace_bytes(int B, int H, int N) { return bwd_layout(B, H, H, N, 64).total; }
 
 // fp8 problem (square): MX-quantized Q, K (codes [B*H*N, d], E8M0 scales
 // [B*H*N, d/32]) and V (transposed 64-key tiles and their scales, as written

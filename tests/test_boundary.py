@@ -298,3 +298,35 @@ def test_binding_tensor_checks_on_host():
         _check("t", t, cpu, torch.bfloat16, (2, 3, 5, 64))
     with pytest.raises(ValueError, match="bytes"):
         _check("t", t, cpu, min_bytes=t.numel() * 2 + 1)
+
+
+def _bwd_gqa_call(**kw):
+    a = dict(q=A, k=A + 8 * MB, v=A + 12 * MB, o=A + 16 * MB, dout=A + 24 * MB, lse=A + 32 * MB,
+             dq=A + 40 * MB, dk=A + 48 * MB, dv=A + 52 * MB, B=1, H=4, Hkv=2, N=512, d=128,
+             scale=0.125, causal=1, ws=A + 64 * MB, ws_bytes=16 * MB, stream=None)
+    a.update(kw)
+    return fa.fa_bwd_gqa(a["q"], a["k"], a["v"], a["o"], a["dout"], a["lse"], a["dq"], a["dk"], a["dv"],
+                         a["B"], a["H"], a["Hkv"], a["N"], a["d"], a["scale"], a["causal"], a["ws"],
+                         a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(Hkv=3), fa.FA_ERR_HEADS), (dict(Hkv=0), fa.FA_ERR_SHAPE), (dict(H=0), fa.FA_ERR_SHAPE),
+    (dict(k=None), fa.FA_ERR_NULL), (dict(dv=None), fa.FA_ERR_NULL),
+    (dict(d=96), fa.FA_ERR_UNSUPPORTED_D),
+    (dict(ws_bytes=1024), fa.FA_ERR_WORKSPACE),
+    # k, v, dk, dv are [B, Hkv, N, d]: 256 KB each here
+    (dict(dk=A + 8 * MB + 128 * 1024), fa.FA_ERR_ALIAS), (dict(dv=A + 48 * MB + 4096), fa.FA_ERR_ALIAS),
+    (dict(ws=A + 40 * MB + 64), fa.FA_ERR_ALIAS),
+])
+def test_bwd_gqa_bad_arguments_rejected_on_host(kw, status):
+    assert _bwd_gqa_call(**kw) == status
+
+
+def test_bwd_gqa_workspace_size():
+    d_part = (1 * 4 * 512 * 4 + 255) // 256 * 256
+    assert fa.fa_bwd_gqa_workspace_size(1, 4, 4, 512, 128) == fa.fa_bwd_workspace_size(1, 4, 512, 128) == d_part
+    # per-query-head fp32 partial dK and dV for a shared K/V head
+    assert fa.fa_bwd_gqa_workspace_size(1, 4, 2, 512, 128) == d_part + 2 * 4 * 512 * 128 * 4
+    assert fa.fa_bwd_gqa_workspace_size(1, 4, 3, 512, 128) == 0
+    assert fa.fa_bwd_gqa_workspace_size(1, 4, 2, 512, 80) == 0
