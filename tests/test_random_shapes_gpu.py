@@ -8,8 +8,9 @@ and queries (queries at most the keys when causal, as the entry points
 require); 1 to 8 key chunks; one or two batches; inputs scaled so that some
 rows' scores are far from 1.  Each problem runs through fa_fwd_gqa, the
 square multi-head ones also through fa_fwd, fa_fwd_splitkv and (the
-even-numbered ones) fa_bwd, and every output is compared element by
-element with the fp64 oracle at the bf16 tolerances."""
+even-numbered ones) fa_bwd, the even-numbered square grouped ones through
+fa_bwd_gqa, and every output is compared element by element with the fp64
+oracle at the bf16 tolerances."""
 import math
 
 import numpy as np
@@ -68,7 +69,11 @@ def test_random_shape(i, B, H, Hkv, Nq, Nk, d, causal, splits, amp):
     o, lse = fa.fwd_gqa(qd, kd, vd, scale=scale, causal=causal, num_splits=splits)
     torch.cuda.synchronize()
     assert_close(*_np(o, lse), O_ref, L_ref, "bf16", "fa_fwd_gqa " + case)
-    if Hkv != H or Nq != Nk:
+    if Nq != Nk:
+        return
+    if Hkv != H:
+        if i % 2 == 0:
+            _check_bwd(fa, torch, fa.bwd_gqa, q, k, v, qd, kd, vd, o, lse, rng, scale, causal, case)
         return
     o, lse = fa.fwd(qd, kd, vd, scale=scale, causal=causal)
     torch.cuda.synchronize()
@@ -76,14 +81,24 @@ def test_random_shape(i, B, H, Hkv, Nq, Nk, d, causal, splits, amp):
     o2, lse2 = fa.fwd_splitkv(qd, kd, vd, scale=scale, causal=causal, num_splits=splits)
     torch.cuda.synchronize()
     assert_close(*_np(o2, lse2), O_ref, L_ref, "bf16", "fa_fwd_splitkv " + case)
-    if i % 2:
-        return
-    g = _bf((B, H, Nq, d), rng, 1.0)
-    dq, dk, dv = fa.bwd(qd, kd, vd, o, lse, upload(g, "bf16"), scale=scale, causal=causal)
+    if i % 2 == 0:
+        _check_bwd(fa, torch, fa.bwd, q, k, v, qd, kd, vd, o, lse, rng, scale, causal, case)
+
+
+def _check_bwd(fa, torch, fn, q, k, v, qd, kd, vd, o, lse, rng, scale, causal, case):
+    """Gradients through fn against the oracle's: the square backward on K/V
+    repeated once per query head of a group, dK and dV summed per group."""
+    B, H, N, d = q.shape
+    Hkv = k.shape[1]
+    G = H // Hkv
+    g = _bf((B, H, N, d), rng, 1.0)
+    dq, dk, dv = fn(qd, kd, vd, o, lse, upload(g, "bf16"), scale=scale, causal=causal)
     torch.cuda.synchronize()
-    ref = oracle.attention_bwd_c(q, k, v, g, scale, causal)
+    dQ, dKr, dVr = oracle.attention_bwd_c(q, np.repeat(k, G, axis=1), np.repeat(v, G, axis=1), g, scale,
+                                          causal)
+    ref = (dQ, dKr.reshape(B, Hkv, G, N, d).sum(axis=2), dVr.reshape(B, Hkv, G, N, d).sum(axis=2))
     for name, t, r in zip(("dQ", "dK", "dV"), (dq, dk, dv), ref):
         got = t.float().cpu().numpy().astype(np.float64)
         err, mx = float(np.abs(got - r).max()), float(np.abs(r).max())
-        note("fa_bwd %s %s: max|err|=%.3e max|ref|=%.3e" % (name, case, err, mx))
-        assert err <= 2e-2 * mx, "fa_bwd %s %s" % (name, case)
+        note("%s %s %s: max|err|=%.3e max|ref|=%.3e" % (fn.__name__, name, case, err, mx))
+        assert err <= 2e-2 * mx, "%s %s %s" % (fn.__name__, name, case)
