@@ -368,14 +368,17 @@ def bwd_bench(fa, args, w, x):
 
 
 def fp8_bench(fa, args, w, x):
-    """Time fa_fwd_fp8 on the workload's quantized inputs; returns the JSON line."""
+    """Time fa_fwd_fp8 on the workload's quantized inputs (fa_fwd_fp8_gqa with
+    --hkv: K and V keep the workload's first HKV heads); returns the JSON line."""
     import torch
     dev = torch.device("cuda:0")
 
     def up(bits):
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
 
+    hkv = args.hkv or w.H
     q, k, v = up(x["q_bits"]), up(x["k_bits"]), up(x["v_bits"])
+    k, v = k[:, :hkv].contiguous(), v[:, :hkv].contiguous()
     stream = torch.cuda.current_stream(dev)
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     ev[0].record(stream)
@@ -387,12 +390,14 @@ def fp8_bench(fa, args, w, x):
     quant_ms = ev[0].elapsed_time(ev[1])
     o = torch.empty_like(q)
     lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
-    a = (q8.data_ptr(), qs.data_ptr(), k8.data_ptr(), ks.data_ptr(), v8t.data_ptr(), vs.data_ptr(),
-         o.data_ptr(), lse.data_ptr(), w.B, w.H, w.N, w.d, w.scale, int(w.causal), stream.cuda_stream)
+    heads = (w.B, w.H, hkv) if args.hkv else (w.B, w.H)
+    a = ((q8.data_ptr(), qs.data_ptr(), k8.data_ptr(), ks.data_ptr(), v8t.data_ptr(), vs.data_ptr(),
+          o.data_ptr(), lse.data_ptr()) + heads + (w.N, w.d, w.scale, int(w.causal), stream.cuda_stream))
+    call = fa.fa_fwd_fp8_gqa if args.hkv else fa.fa_fwd_fp8
     for _ in range(args.warmup):
-        st = fa.fa_fwd_fp8(*a)
+        st = call(*a)
         if st != 0:
-            raise fa.FaError(st, "fa_fwd_fp8")
+            raise fa.FaError(st, call.__name__)
     torch.cuda.synchronize()
     if not (torch.isfinite(lse).all() and torch.isfinite(o.float()).all()):
         raise RuntimeError("non-finite output")
@@ -400,7 +405,7 @@ def fp8_bench(fa, args, w, x):
     t0 = time.perf_counter()
     ev0.record(stream)
     for _ in range(args.steps):
-        fa.fa_fwd_fp8(*a)
+        call(*a)
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -411,8 +416,9 @@ def fp8_bench(fa, args, w, x):
             "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall * 1e3 / args.steps, 4),
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp8_e4m3",
             "data": "synthetic (seeded N(0,1) draws, bf16-rounded, then MX E4M3 block-quantized)",
-            "config": {"workload": w.name + "_fp8", "B": w.B, "H": w.H, "N": w.N, "d": w.d,
-                       "causal": w.causal, "flops": w.flops, "entry_point": "fa_fwd_fp8",
+            "config": {"workload": w.name + "_fp8" + ("_hkv%d" % hkv if args.hkv else ""), "B": w.B,
+                       "H": w.H, "Hkv": hkv, "N": w.N, "d": w.d, "causal": w.causal, "flops": w.flops,
+                       "entry_point": "fa_fwd_fp8_gqa" if args.hkv else "fa_fwd_fp8",
                        "quantize_ms": round(quant_ms, 4)},
             "roofline": {"bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_FP8_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(ach / PEAK_FP8_TFLOPS, 4), "traffic": None,

@@ -256,6 +256,18 @@ int fa_fwd_fp8(const void* q8, const void* qs, const void* k8, const void* ks, c
                const void* vs, void* o, float* lse, int B, int H, int N, int d, float scale,
                int causal, hipStream_t stream);
 
+/*
+ * fp8 forward with grouped K/V heads (MQA/GQA, as fa_fwd_gqa with
+ * Nq = Nk = N): q8, qs for the [B*H*N, d] rows of Q; k8, ks for the
+ * [B*Hkv*N, d] rows of K and v8t, vs for the B*Hkv heads of V, as the
+ * quantizers write them; query head h of batch b reads K/V head
+ * h / (H / Hkv) of batch b.  Hkv == H is fa_fwd_fp8.  Errors as for
+ * fa_fwd_fp8, plus FA_ERR_HEADS when Hkv does not divide H.
+ */
+int fa_fwd_fp8_gqa(const void* q8, const void* qs, const void* k8, const void* ks, const void* v8t,
+                   const void* vs, void* o, float* lse, int B, int H, int Hkv, int N, int d,
+                   float scale, int causal, hipStream_t stream);
+
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* fa_strerror(int status);
 

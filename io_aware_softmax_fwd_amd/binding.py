@@ -25,6 +25,8 @@ Low level (same names and arguments as the C functions, raw pointers):
     fa_fp8_v_bytes(BH, N, d), fa_fp8_v_scale_bytes(BH, N, d)   -> bytes
     fa_fwd_fp8(q8, qs, k8, ks, v8t, vs, o, lse, B, H, N, d, scale, causal,
                stream)                                         -> status
+    fa_fwd_fp8_gqa(q8, qs, k8, ks, v8t, vs, o, lse, B, H, Hkv, N, d, scale,
+                   causal, stream)                             -> status
     fa_strerror(status)                                        -> str
 High level (torch tensors on a ROCm device):
     fwd(q, k, v, scale=None, causal=False, out=None, lse=None) -> (o, lse)
@@ -65,7 +67,7 @@ FA_ERR_HEADS = 11
 EXPORTED = ("fa_fwd", "fa_fwd_f32", "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_size",
             "fa_fwd_splitkv_num_splits", "fa_fwd_gqa", "fa_fwd_gqa_num_splits", "fa_bwd",
             "fa_bwd_workspace_size", "fa_bwd_gqa", "fa_bwd_gqa_workspace_size", "fa_quantize_qk_fp8", "fa_quantize_v_fp8", "fa_fp8_v_bytes",
-            "fa_fp8_v_scale_bytes", "fa_fwd_fp8", "fa_strerror")
+            "fa_fp8_v_scale_bytes", "fa_fwd_fp8", "fa_fwd_fp8_gqa", "fa_strerror")
 
 _lib = None
 
@@ -157,6 +159,9 @@ def load():
     lib.fa_fwd_fp8.restype = ctypes.c_int
     lib.fa_fwd_fp8.argtypes = ([ctypes.c_void_p] * 8 + [ctypes.c_int] * 4 +
                                [ctypes.c_float, ctypes.c_int, ctypes.c_void_p])
+    lib.fa_fwd_fp8_gqa.restype = ctypes.c_int
+    lib.fa_fwd_fp8_gqa.argtypes = ([ctypes.c_void_p] * 8 + [ctypes.c_int] * 5 +
+                                   [ctypes.c_float, ctypes.c_int, ctypes.c_void_p])
     lib.fa_strerror.restype = ctypes.c_char_p
     lib.fa_strerror.argtypes = [ctypes.c_int]
     _lib = lib
@@ -233,6 +238,10 @@ def fa_fp8_v_scale_bytes(BH, N, d):
 
 def fa_fwd_fp8(q8, qs, k8, ks, v8t, vs, o, lse, B, H, N, d, scale, causal, stream):
     return load().fa_fwd_fp8(q8, qs, k8, ks, v8t, vs, o, lse, B, H, N, d, scale, causal, stream)
+
+
+def fa_fwd_fp8_gqa(q8, qs, k8, ks, v8t, vs, o, lse, B, H, Hkv, N, d, scale, causal, stream):
+    return load().fa_fwd_fp8_gqa(q8, qs, k8, ks, v8t, vs, o, lse, B, H, Hkv, N, d, scale, causal, stream)
 
 
 def fa_strerror(status):
@@ -475,8 +484,9 @@ def quantize_v_fp8(v, stream=None):
 
 def fwd_fp8(q8, qs, k8, ks, v8t, vs, scale=None, causal=False, stream=None):
     """fp8 attention forward of quantized inputs (as returned by
-    quantize_qk_fp8 and quantize_v_fp8); q8 gives the [B,H,N,d] shape.
-    Returns (o bf16 [B,H,N,d], lse fp32 [B,H,N])."""
+    quantize_qk_fp8 and quantize_v_fp8); q8 gives the [B,H,N,d] shape and
+    k8 [B,Hkv,N,d] the K/V heads (Hkv dividing H; Hkv < H reads each K/V head
+    for H/Hkv query heads).  Returns (o bf16 [B,H,N,d], lse fp32 [B,H,N])."""
     import torch
     dev = _gpu_device("q8", q8)
     _check("q8", q8, dev, torch.uint8)
@@ -485,20 +495,24 @@ def fwd_fp8(q8, qs, k8, ks, v8t, vs, scale=None, causal=False, stream=None):
     B, H, N, d = q8.shape
     if d not in (64, 128):
         raise ValueError("head dimension must be 64 or 128")
-    _check("k8", k8, dev, torch.uint8, (B, H, N, d))
-    for name, t in (("qs", qs), ("ks", ks)):
-        _check(name, t, dev, torch.uint8, (B, H, N, d // 32))
-    _check("v8t", v8t, dev, torch.uint8, min_bytes=fa_fp8_v_bytes(B * H, N, d))
-    _check("vs", vs, dev, torch.uint8, min_bytes=fa_fp8_v_scale_bytes(B * H, N, d))
+    _gpu_device("k8", k8)
+    if k8.dim() != 4:
+        raise ValueError("k8 must be [B, Hkv, N, d]")
+    Hkv = k8.shape[1]
+    _check("k8", k8, dev, torch.uint8, (B, Hkv, N, d))
+    _check("qs", qs, dev, torch.uint8, (B, H, N, d // 32))
+    _check("ks", ks, dev, torch.uint8, (B, Hkv, N, d // 32))
+    _check("v8t", v8t, dev, torch.uint8, min_bytes=fa_fp8_v_bytes(B * Hkv, N, d))
+    _check("vs", vs, dev, torch.uint8, min_bytes=fa_fp8_v_scale_bytes(B * Hkv, N, d))
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     o = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=q8.device)
     lse = torch.empty((B, H, N), dtype=torch.float32, device=q8.device)
     if stream is None:
         stream = torch.cuda.current_stream(q8.device).cuda_stream
-    st = fa_fwd_fp8(q8.data_ptr(), qs.data_ptr(), k8.data_ptr(), ks.data_ptr(), v8t.data_ptr(),
-                    vs.data_ptr(), o.data_ptr(), lse.data_ptr(), B, H, N, d, float(scale),
-                    int(bool(causal)), stream)
+    st = fa_fwd_fp8_gqa(q8.data_ptr(), qs.data_ptr(), k8.data_ptr(), ks.data_ptr(), v8t.data_ptr(),
+                        vs.data_ptr(), o.data_ptr(), lse.data_ptr(), B, H, Hkv, N, d, float(scale),
+                        int(bool(causal)), stream)
     if st != FA_OK:
-        raise FaError(st, "fa_fwd_fp8")
+        raise FaError(st, "fa_fwd_fp8_gqa")
     return o, lse

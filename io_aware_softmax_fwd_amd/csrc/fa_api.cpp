@@ -289,10 +289,12 @@ int fa_quantize_v_fp8(const void* v, int BH, int N, int d, void* v8t, void* vs, 
   return fa::launch_quantize_v_fp8(v, BH, N, d, v8t, vs, stream) == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
-int fa_fwd_fp8(const void* q8, const void* qs, const void* k8, const void* ks, const void* v8t, const void* vs,
-               void* o, float* lse, int B, int H, int N, int d, float scale, int causal, hipStream_t stream) {
+int fa_fwd_fp8_gqa(const void* q8, const void* qs, const void* k8, const void* ks, const void* v8t,
+                   const void* vs, void* o, float* lse, int B, int H, int Hkv, int N, int d, float scale,
+                   int causal, hipStream_t stream) {
   if (!q8 || !qs || !k8 || !ks || !v8t || !vs || !o || !lse) return FA_ERR_NULL;
-  if (B < 1 || H < 1 || N < 1) return FA_ERR_SHAPE;
+  if (B < 1 || H < 1 || Hkv < 1 || N < 1) return FA_ERR_SHAPE;
+  if (H % Hkv != 0) return FA_ERR_HEADS;
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED_D;
   const int64_t rows = (int64_t)B * H * N;
   if (rows * d >= kMaxElems || (int64_t)N * d * 2 >= (int64_t(1) << 31) || grid_too_large((int64_t)B * H, N))
@@ -300,13 +302,20 @@ int fa_fwd_fp8(const void* q8, const void* qs, const void* k8, const void* ks, c
   if (!(scale > 0.f) || !isfinite(scale)) return FA_ERR_SCALE;
   if (causal != 0 && causal != 1) return FA_ERR_CAUSAL;
   if (any_misaligned({q8, qs, k8, ks, v8t, vs, o, lse})) return FA_ERR_ALIGN;
-  const int64_t cb = rows * d, sb = rows * (d / 32), ob = rows * d * 2, lb = rows * 4,
-                vcb = fa::fp8_v_code_bytes((int64_t)B * H, N, d), vsb = fa::fp8_v_scale_bytes((int64_t)B * H, N, d);
+  const int64_t kvrows = (int64_t)B * Hkv * N;
+  const int64_t cb = rows * d, sb = rows * (d / 32), kcb = kvrows * d, ksb = kvrows * (d / 32),
+                ob = rows * d * 2, lb = rows * 4, vcb = fa::fp8_v_code_bytes((int64_t)B * Hkv, N, d),
+                vsb = fa::fp8_v_scale_bytes((int64_t)B * Hkv, N, d);
   const std::initializer_list<std::pair<const void*, int64_t>> ins = {
-      {q8, cb}, {qs, sb}, {k8, cb}, {ks, sb}, {v8t, vcb}, {vs, vsb}};
+      {q8, cb}, {qs, sb}, {k8, kcb}, {ks, ksb}, {v8t, vcb}, {vs, vsb}};
   if (any_overlap(o, ob, ins) || any_overlap(lse, lb, ins) || overlap(o, ob, lse, lb)) return FA_ERR_ALIAS;
-  const fa::Fp8Problem p{q8, qs, k8, ks, v8t, vs, o, lse, B, H, N, d, scale, causal};
+  const fa::Fp8Problem p{q8, qs, k8, ks, v8t, vs, o, lse, B, H, Hkv, N, d, scale, causal};
   return fa::launch_fwd_fp8(p, stream) == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+int fa_fwd_fp8(const void* q8, const void* qs, const void* k8, const void* ks, const void* v8t, const void* vs,
+               void* o, float* lse, int B, int H, int N, int d, float scale, int causal, hipStream_t stream) {
+  return fa_fwd_fp8_gqa(q8, qs, k8, ks, v8t, vs, o, lse, B, H, H, N, d, scale, causal, stream);
 }
 
 const char* fa_strerror(int status) {

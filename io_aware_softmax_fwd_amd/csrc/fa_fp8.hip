@@ -343,7 +343,7 @@ __global__ __launch_bounds__(kF8Threads, 2) void fwd_fp8_kernel(
     const unsigned char* __restrict__ k8, const unsigned char* __restrict__ ks,
     const unsigned char* __restrict__ v8t, const unsigned char* __restrict__ vs,
     unsigned short* __restrict__ o, float* __restrict__ lse, int N, int BH, int n_qtiles, float scale,
-    int hg) {
+    int hg, int H, int G) {
   using F = FwdF8<D, CAUSAL>;
   using C = F8Cfg<D>;
   __shared__ __attribute__((aligned(1024))) unsigned char k_lds0[C::kTile];
@@ -364,10 +364,12 @@ __global__ __launch_bounds__(kF8Threads, 2) void fwd_fp8_kernel(
   f.kbuf[1] = k_lds1;
   f.vbuf[0] = v_lds0;
   f.vbuf[1] = v_lds1;
-  f.kh = k8 + (int64_t)bh * N * D;
-  f.ksh = ks + (int64_t)bh * N * (D / 32);
-  f.vth = v8t + (int64_t)bh * T * D * kF8Keys;
-  f.vsh = vs + (int64_t)bh * T * 2 * 32 * (D / 32);
+  // K/V head of this query head (G query heads share one)
+  const int64_t kvh = (int64_t)(bh / H) * (H / G) + (bh % H) / G;
+  f.kh = k8 + kvh * N * D;
+  f.ksh = ks + kvh * N * (D / 32);
+  f.vth = v8t + kvh * T * D * kF8Keys;
+  f.vsh = vs + kvh * T * 2 * 32 * (D / 32);
   f.N = N;
   f.wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   f.l32 = lane & 31;
@@ -489,7 +491,8 @@ hipError_t launch_fp8(const Fp8Problem& p, hipStream_t stream) {
                      static_cast<const unsigned char*>(p.qs), static_cast<const unsigned char*>(p.k8),
                      static_cast<const unsigned char*>(p.ks), static_cast<const unsigned char*>(p.v8t),
                      static_cast<const unsigned char*>(p.vs), static_cast<unsigned short*>(p.o), p.lse, p.N,
-                     BH, n_qtiles, p.scale, xcd_head_group(BH, n_qtiles, 1, CAUSAL ? n_qtiles : 0, 1));
+                     BH, n_qtiles, p.scale, xcd_head_group(BH, n_qtiles, 1, CAUSAL ? n_qtiles : 0, 1),
+                     p.H, p.H / p.Hkv);
   return hipGetLastError();
 }
 

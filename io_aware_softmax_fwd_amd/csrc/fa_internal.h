@@ -83,7 +83,7 @@ struct Fp8Problem {
   const void* vs;
   void* o;
   float* lse;
-  int B, H, N, d;
+  int B, H, Hkv, N, d;   // K and V of B*Hkv heads; query head h reads K/V head h / (H/Hkv)
   float scale;
   int causal;
 };

@@ -330,3 +330,15 @@ def test_bwd_gqa_workspace_size():
     assert fa.fa_bwd_gqa_workspace_size(1, 4, 2, 512, 128) == d_part + 2 * 4 * 512 * 128 * 4
     assert fa.fa_bwd_gqa_workspace_size(1, 4, 3, 512, 128) == 0
     assert fa.fa_bwd_gqa_workspace_size(1, 4, 2, 512, 80) == 0
+
+
+def test_fwd_fp8_gqa_checks_on_host():
+    a = dict(q8=A, qs=A + 8 * MB, k8=A + 16 * MB, ks=A + 24 * MB, v8t=A + 32 * MB, vs=A + 40 * MB,
+             o=A + 48 * MB, lse=A + 56 * MB, B=1, H=4, Hkv=2, N=64, d=64, scale=0.125, causal=0, stream=None)
+    call = lambda **kw: fa.fa_fwd_fp8_gqa(*[dict(a, **kw)[n] for n in (
+        "q8", "qs", "k8", "ks", "v8t", "vs", "o", "lse", "B", "H", "Hkv", "N", "d", "scale", "causal", "stream")])
+    assert call(Hkv=3) == fa.FA_ERR_HEADS
+    assert call(Hkv=0) == fa.FA_ERR_SHAPE
+    assert call(k8=None) == fa.FA_ERR_NULL
+    # K codes of B*Hkv*N rows (8 KB here): an output 4 KB in overlaps them
+    assert call(o=A + 16 * MB + 4096) == fa.FA_ERR_ALIAS

@@ -247,3 +247,49 @@ def test_fp8_offset_moves(d, causal):
     O, L = _run_fp8(*_gpu_quant(q, k, v), 1.0, causal)
     _, deq = _oracle_quant(q, k, v)
     _check_rows(O, L, deq, 1.0, causal, np.arange(H * N), case)
+
+
+@pytest.mark.parametrize("B,H,Hkv,N,d,causal", [(1, 8, 2, 300, 128, True), (2, 4, 1, 257, 64, False)])
+def test_fp8_grouped_kv_heads(B, H, Hkv, N, d, causal):
+    """fa_fwd_fp8_gqa: query head h reads K/V head h / (H/Hkv).  Against the
+    oracle on the dequantized inputs with K/V repeated per query head, and bit
+    for bit against fa_fwd_fp8 on the repeated quantized K/V."""
+    torch = torch_or_skip()
+    import io_aware_softmax_fwd_amd as fa
+    G = H // Hkv
+    case = "fp8 gqa B=%d H=%d Hkv=%d N=%d d=%d causal=%d" % (B, H, Hkv, N, d, causal)
+    note(case)
+    q = _bf((B, H, N, d), 70 + N + d)
+    k, v = _bf((B, Hkv, N, d), 71 + N + d), _bf((B, Hkv, N, d), 72 + N + d)
+    scale = float(np.float32(1 / math.sqrt(d)))
+    q8, qs, k8, ks, v8t, vs = _gpu_quant_heads(q, k, v)
+    O, L = _run_fp8(q8, qs, k8, ks, v8t, vs, scale, causal)
+    # oracle side: dequantized K/V of the Hkv heads, repeated for each query head
+    qc, qsc = mx.mx_quantize(q, axis=-1)
+    kc, ksc = mx.mx_quantize(k, axis=-1)
+    T = (N + 63) // 64
+    vp = np.zeros((B * Hkv, T * 64, d), dtype=np.float32)
+    vp[:, :N] = v.reshape(B * Hkv, N, d)
+    vc, vsc = mx.mx_quantize(vp, axis=-2)
+    vdq = mx.mx_dequantize(vc, vsc, axis=-2)[:, :N].reshape(B, Hkv, N, d)
+    deq = (mx.mx_dequantize(qc, qsc), np.repeat(mx.mx_dequantize(kc, ksc), G, axis=1), np.repeat(vdq, G, axis=1))
+    _check_rows(O, L, deq, scale, causal, np.arange(B * H * N), case)
+    # the same bits as the multi-head kernel on repeated codes and scales
+    rep = lambda t: t.reshape(B, Hkv, -1).repeat_interleave(G, dim=1).reshape(-1).contiguous()
+    o2, l2 = fa.fwd_fp8(q8, qs, k8.repeat_interleave(G, dim=1).contiguous(),
+                        ks.repeat_interleave(G, dim=1).contiguous(), rep(v8t), rep(vs),
+                        scale=scale, causal=causal)
+    torch.cuda.synchronize()
+    assert np.array_equal(o2.float().cpu().numpy(), O.astype(np.float32)) and \
+        np.array_equal(l2.cpu().numpy(), L.astype(np.float32))
+
+
+def _gpu_quant_heads(q, k, v):
+    """GPU quantization of q [B,H,N,d] and k, v [B,Hkv,N,d]."""
+    torch = torch_or_skip()
+    import io_aware_softmax_fwd_amd as fa
+    q8, qs = fa.quantize_qk_fp8(upload(q, "bf16"))
+    k8, ks = fa.quantize_qk_fp8(upload(k, "bf16"))
+    v8t, vs = fa.quantize_v_fp8(upload(v, "bf16"))
+    torch.cuda.synchronize()
+    return q8, qs, k8, ks, v8t, vs
