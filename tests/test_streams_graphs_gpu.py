@@ -93,3 +93,58 @@ def test_graph_replays_match_eager():
         same = [_same_bits(torch, a, b) for a, b in zip(got, want)]
         note("replay %d: bitwise equal to eager: %s" % (rep, dict(zip(names, same))))
         assert all(same), "replay %d differs from the eager calls" % rep
+
+
+def test_graph_replays_match_eager_grouped_and_fp8():
+    """The same for a grouped-K/V-head step: fa_fwd_gqa with 4 key chunks,
+    fa_bwd_gqa (its per-head fp32 shares and group sum live in the
+    workspace), and the fp8 quantizers followed by fa_fwd_fp8_gqa."""
+    torch = torch_or_skip()
+    import io_aware_softmax_fwd_amd as fa
+    B, H, Hkv, N, d = 1, 8, 2, 500, 128
+    note("graph capture: fa_fwd_gqa (4 chunks), fa_bwd_gqa, fp8 quantizers + fa_fwd_fp8_gqa; "
+         "B=%d H=%d Hkv=%d N=%d d=%d causal" % (B, H, Hkv, N, d))
+
+    def bf(seed, heads):
+        x = np.random.default_rng(seed).standard_normal((B, heads, N, d), dtype=np.float32)
+        return upload(W.bf16_bits_to_f32(W.bf16_bits_rne(x)), "bf16")
+
+    q, k, v, g = bf(51, H), bf(52, Hkv), bf(53, Hkv), bf(54, H)
+    ws_f = torch.empty(fa.fa_fwd_splitkv_workspace_size(B, H, N, d, 4), dtype=torch.uint8, device="cuda")
+    ws_b = torch.empty(fa.fa_bwd_gqa_workspace_size(B, H, Hkv, N, d), dtype=torch.uint8, device="cuda")
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+
+    def step():
+        fa.fwd_gqa(q, k, v, causal=True, num_splits=4, workspace=ws_f, out=o, lse=lse)
+        grads = fa.bwd_gqa(q, k, v, o, lse, g, causal=True, workspace=ws_b)
+        q8, qs = fa.quantize_qk_fp8(q)
+        k8, ks = fa.quantize_qk_fp8(k)
+        v8t, vs = fa.quantize_v_fp8(v)
+        o8, l8 = fa.fwd_fp8(q8, qs, k8, ks, v8t, vs, causal=True)
+        return [o, lse] + list(grads) + [o8, l8]
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        captured = step()
+    for rep in range(3):
+        for t, seed, heads in zip((q, k, v, g), (100 * rep + 61, 100 * rep + 62, 100 * rep + 63, 100 * rep + 64),
+                                  (H, Hkv, Hkv, H)):
+            t.copy_(bf(seed, heads))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = [t.clone() for t in captured]
+        x = torch.randn(512, 512, device="cuda")
+        (x @ x).sum().item()
+        want = step()
+        torch.cuda.synchronize()
+        same = [_same_bits(torch, a, b) for a, b in zip(got, want)]
+        note("replay %d: bitwise equal to eager: %s" % (rep, same))
+        assert all(same), "replay %d differs from the eager calls" % rep
