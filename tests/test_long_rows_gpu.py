@@ -62,3 +62,30 @@ def test_long_rows(d, causal):
     O = o.float().cpu().numpy().astype(np.float64).reshape(-1, d)[rows]
     L = lse.cpu().numpy().astype(np.float64).reshape(-1)[rows]
     assert_close(O, L, O_ref, L_ref, "bf16", "fa_fwd_splitkv long rows d=%d causal=%d splits=%d" % (d, causal, splits))
+
+
+@pytest.mark.parametrize("Hkv", [1, 8, 32])
+def test_decode_full_size(Hkv):
+    """The decoding step the benchmark times, at its size: one query row for
+    each of 32 heads against 131072 keys (d=128, causal), K/V shared by
+    32/Hkv query heads, with the chunk count the library suggests for this
+    GPU (256 chunks for one K/V head).  Every row against the oracle."""
+    torch = torch_or_skip()
+    import io_aware_softmax_fwd_amd as fa
+    B, H, d, nk = 1, 32, 128, N
+    rng = np.random.default_rng(8300 + Hkv)
+    rt = lambda x: W.bf16_bits_to_f32(W.bf16_bits_rne(x))
+    q = rt(rng.standard_normal((B, H, 1, d), dtype=np.float32))
+    k = rt(rng.standard_normal((B, Hkv, nk, d), dtype=np.float32))
+    v = rt(rng.standard_normal((B, Hkv, nk, d), dtype=np.float32))
+    scale = float(np.float32(1 / math.sqrt(d)))
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    splits = fa.fa_fwd_gqa_num_splits(B, H, Hkv, 1, nk, 1, cus)
+    note("decode full size: H=%d Hkv=%d Nk=%d d=%d causal, %d chunks" % (H, Hkv, nk, d, splits))
+    o, lse = fa.fwd_gqa(upload(q, "bf16"), upload(k, "bf16"), upload(v, "bf16"), scale=scale, causal=True,
+                        num_splits=splits)
+    torch.cuda.synchronize()
+    O_ref, L_ref = oracle.attention_c(q, k, v, scale, True)
+    O = o.float().cpu().numpy().astype(np.float64)
+    L = lse.cpu().numpy().astype(np.float64)
+    assert_close(O, L, O_ref, L_ref, "bf16", "fa_fwd_gqa decode Hkv=%d splits=%d" % (Hkv, splits))
