@@ -148,3 +148,49 @@ def test_graph_replays_match_eager_grouped_and_fp8():
         same = [_same_bits(torch, a, b) for a, b in zip(got, want)]
         note("replay %d: bitwise equal to eager: %s" % (rep, same))
         assert all(same), "replay %d differs from the eager calls" % rep
+
+
+def test_concurrent_host_threads():
+    """The library keeps no state between calls: two host threads, each on
+    its own stream, call fa_fwd, fa_fwd_gqa (key split) and fa_bwd at the same
+    time, and every result equals the one computed alone."""
+    torch = torch_or_skip()
+    import threading
+    import io_aware_softmax_fwd_amd as fa
+    note("concurrent host threads: fa_fwd, fa_fwd_gqa (3 chunks), fa_bwd on two streams")
+    probs = []
+    for t in range(2):
+        q, k, v, g = _bf(300 + 4 * t), _bf(301 + 4 * t), _bf(302 + 4 * t), _bf(303 + 4 * t)
+        probs.append((q, k, v, g))
+
+    def run(q, k, v, g, stream=None):
+        o, lse = fa.fwd(q, k, v, causal=True, stream=stream)
+        o2, lse2 = fa.fwd_gqa(q, k[:, :2].contiguous(), v[:, :2].contiguous(), causal=True, num_splits=3,
+                              stream=stream)
+        dq, dk, dv = fa.bwd(q, k, v, o, lse, g, causal=True, stream=stream)
+        return [o, lse, o2, lse2, dq, dk, dv]
+
+    alone = [run(*p) for p in probs]
+    torch.cuda.synchronize()
+    results = [None, None]
+    errors = []
+
+    def worker(i):
+        try:
+            s = torch.cuda.Stream()
+            with torch.cuda.stream(s):
+                for _ in range(5):
+                    results[i] = run(*probs[i], stream=s.cuda_stream)
+            s.synchronize()
+        except Exception as e:   # reported below, on the main thread
+            errors.append(e)
+
+    threads = [threading.Thread(target=worker, args=(i,)) for i in range(2)]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for i in range(2):
+        assert all(_same_bits(torch, a, b) for a, b in zip(results[i], alone[i])), "thread %d differs" % i
