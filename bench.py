@@ -3,12 +3,20 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 4]
 
 One step is one fa_fwd call over the whole workload (all query rows of all
-heads) with Q, K, V already resident in device memory.  W untimed steps are
-followed by K timed steps between two device synchronisations; the kernel's
-own average duration is taken from HIP events recorded on the stream the
-kernel is queued on.  Prints one JSON line.  The defaults (300 and 300)
-give the GPU's clock time to settle under the sustained load: a few
-milliseconds of warm-up leave short kernels timed at a lower clock.
+heads) with Q, K, V already resident in device memory.  W untimed warm-up
+steps are followed by K timed steps between two device synchronisations; the
+kernel's own average duration is taken from HIP events recorded on the
+stream the kernel is queued on.  Prints one JSON line.
+
+Clock settling: an idle MI355X starts a burst of work at a low graphics
+clock and needs a few tens of milliseconds of sustained load to reach the
+clock its power limit allows (at C4 the first ~20 launches take 2.8 -> 2.03
+ms, the rest 2.00 ms).  So after the W warm-up steps the same step keeps
+running, untimed, until --settle-ms of wall time has passed since the first
+warm-up step (default 1500 ms, 0 turns it off); the line reports how many
+such steps ran ("settle").  The timed region is still exactly K steps.  The
+graphics clock of each XCD and the socket power, read from the driver's
+metrics table (amdsmi) right after the timed steps, go in "gpu_state".
 
 Default workload: B=1, H=32, N=16384, d=128, bf16, causal, with 1% of the Q
 and K rows amplified x8.  Throughput counts 4*B*H*N^2*d FLOPs, halved for
@@ -63,6 +71,9 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 matrix-core peak (published)
 PEAK_FP8_TFLOPS = 5000.0        # MI355X dense fp8 matrix-core peak (published)
+PEAK_FP32_VECTOR_TFLOPS = 157.3  # MI355X fp32 vector peak (published)
+PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E bandwidth (published)
+PEAK_CLOCK_MHZ = 2400.0         # the engine clock the published peaks assume
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fa_fwd_bf16_traffic.json")
 KERNEL_SOURCES = ["fa_fwd_bf16.hip", "fa_device.h", "fa_internal.h", "fa_api.cpp"]
 
@@ -75,17 +86,48 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload_name):
-    """HBM bytes per launch from the committed counter summary, or None if it
-    is missing, for another workload, or taken on different kernel source."""
+def _traffic_table():
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
-        return None
-    if t.get("source_hash") != kernel_source_hash() or t.get("workload") != workload_name:
+        return {}
+    return t if isinstance(t, dict) else {}
+
+
+def measured_traffic(workload_name):
+    """HBM bytes per launch from the committed counter summary, or None if it
+    is missing, has no entry for this workload, or was taken on different
+    kernel source."""
+    t = _traffic_table().get(workload_name)
+    if not t or t.get("source_hash") != kernel_source_hash():
         return None
     return t.get("bytes_per_launch")
+
+
+def io_models(w):
+    """HBM bytes of one launch under the accounting of the IO argument:
+    the algorithmic minimum (Q, K, V read once, O written once, LSE), the
+    standard three-pass attention's 4N^2 + 4Nd elements per head (S written
+    and read, P written and read, plus Q, K, V, O), the tiled pass's
+    8 N^2 d^2 / M elements per head for an on-chip memory of M elements
+    (aiqz.cc Flash Attention IO article, IO complexity section; notes page,
+    sections 3.1 and 3.2), here M = 160 KB of LDS, and this kernel's own
+    model: every 128-row query tile reads the K and V it needs once (only
+    keys up to the diagonal when causal)."""
+    e = w.elem_bytes
+    heads = w.B * w.H
+    m_elems = 160 * 1024 // e
+    tiles = -(-w.N // 128)
+    if w.causal:
+        kv_keys = sum(min(w.N, 128 * (t + 1)) for t in range(tiles))
+    else:
+        kv_keys = tiles * w.N
+    return {"algorithmic": w.algorithmic_bytes,
+            "standard_4N2_4Nd": heads * (4 * w.N * w.N + 4 * w.N * w.d) * e,
+            "tiled_8N2d2_over_M": heads * 8 * w.N * w.N * w.d * w.d / m_elems * e,
+            "kv_per_query_tile": heads * (2 * kv_keys * w.d * e + 2 * w.N * w.d * e + 4 * w.N),
+            "lds_bytes_M": 160 * 1024}
 
 
 def cpu_baseline(x, w, target_s=15.0):
@@ -126,15 +168,53 @@ def copy_calibration(nbytes):
     print(json.dumps({"copy_bytes": nbytes, "launches": 5}))
 
 
+def run_untimed(step, sync, warmup, settle_ms):
+    """W warm-up steps, then more untimed steps until settle_ms of wall time
+    has passed since the first one; returns the number of settle steps."""
+    t0 = time.perf_counter()
+    for _ in range(warmup):
+        step()
+    sync()
+    n = 0
+    while (time.perf_counter() - t0) * 1e3 < settle_ms:
+        for _ in range(8):
+            step()
+        n += 8
+        sync()
+    return n
+
+
+def gpu_state():
+    """Graphics clock of each XCD and socket power from the driver's metrics
+    table (refreshed about once a second), or None where amdsmi is missing."""
+    try:
+        import amdsmi
+        amdsmi.amdsmi_init()
+        h = amdsmi.amdsmi_get_processor_handles()[0]
+        m = amdsmi.amdsmi_get_gpu_metrics_info(h)
+        clks = [int(c) for c in (m.get("current_gfxclks") or []) if isinstance(c, int) and 0 < c < 10000]
+        pw = m.get("current_socket_power")
+        amdsmi.amdsmi_shut_down()
+        if not clks:
+            return None
+        return {"gfx_clock_mhz_per_xcd": clks, "gfx_clock_mhz_mean": round(float(np.mean(clks)), 1),
+                "socket_power_w": pw if isinstance(pw, (int, float)) else None,
+                "source": "amdsmi gpu metrics, read right after the timed steps"}
+    except Exception:   # noqa: BLE001 - an absent or failing metrics reader leaves the field null
+        return None
+
+
 # The profiling session whose output --summarize reads.  Each step is run on
-# the GPU host from the repository root with OUT set to an output folder.
+# the GPU host from the repository root with OUT set to an output folder and
+# WL to the workload id (1..5); the steps whose command holds no --workload
+# are the same for every workload (C4 shapes).
 PROFILE_STEPS = {
     "trace": "rocprofv3 --kernel-trace --stats --output-format csv -d $OUT/trace -o run "
-             "-- python bench.py --no-cpu-baseline",
+             "-- python bench.py --workload $WL --no-cpu-baseline",
     "fetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d $OUT/fetch -o run "
-             "-- python bench.py --steps 3 --warmup 1 --no-cpu-baseline",
+             "-- python bench.py --workload $WL --steps 3 --warmup 1 --settle-ms 0 --no-cpu-baseline",
     "write": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d $OUT/write -o run "
-             "-- python bench.py --steps 3 --warmup 1 --no-cpu-baseline",
+             "-- python bench.py --workload $WL --steps 3 --warmup 1 --settle-ms 0 --no-cpu-baseline",
     "copy_fetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d $OUT/copy_fetch -o run "
                   "-- python bench.py --copy-bytes 268435456",
     "copy_write": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d $OUT/copy_write -o run "
@@ -142,11 +222,11 @@ PROFILE_STEPS = {
     "sq": "rocprofv3 --pmc SQ_WAVE_CYCLES SQ_BUSY_CYCLES SQ_VALU_MFMA_BUSY_CYCLES "
           "SQ_VALU_MFMA_COEXEC_CYCLES SQ_ACTIVE_INST_VALU SQ_WAIT_INST_LDS SQ_WAIT_ANY "
           "SQ_LDS_BANK_CONFLICT GRBM_GUI_ACTIVE --output-format csv -d $OUT/sq -o run "
-          "-- python bench.py --steps 3 --warmup 1 --no-cpu-baseline",
+          "-- python bench.py --workload $WL --steps 3 --warmup 1 --settle-ms 0 --no-cpu-baseline",
     "sq2": "rocprofv3 --pmc SQ_INSTS_VALU SQ_INSTS_MFMA SQ_INSTS_LDS SQ_INSTS_SALU "
            "SQ_ACTIVE_INST_LDS SQ_INSTS_VALU_TRANS_F32 SQ_ACTIVE_INST_ANY GRBM_GUI_ACTIVE "
            "--output-format csv -d $OUT/sq2 -o run "
-           "-- python bench.py --steps 3 --warmup 1 --no-cpu-baseline",
+           "-- python bench.py --workload $WL --steps 3 --warmup 1 --settle-ms 0 --no-cpu-baseline",
     "decode_gqa": "rocprofv3 --kernel-trace --stats --output-format csv -d $OUT/decode_gqa -o run "
                   "-- python bench.py --decode 131072 --hkv 8",
     "decode_mha": "rocprofv3 --kernel-trace --stats --output-format csv -d $OUT/decode_mha -o run "
@@ -167,8 +247,14 @@ TRACE_ONLY = {"decode_gqa": "fa_fwd_gqa_decode_b1_h32_hkv8_nk131072_d128",
               "bwd": "fa_bwd_bf16_n16k_d128_causal_amplified",
               "fp8": "fa_fwd_fp8_bf16_n16k_d128_causal_amplified",
               "gqa": "fa_fwd_gqa_hkv8_bf16_n16k_d128_causal_amplified"}
-KERNEL_KEY = "fwd_bf16_kernel"
+# the forward kernels of fa_fwd and fa_fwd_f32 (the summary's own kernel)
+KERNEL_KEY = "fa::(anonymous namespace)::fwd_"
 COPY_KEY = "copy"
+
+
+def profile_command(step, wl):
+    """The command of one profiling step for workload id wl, as run."""
+    return PROFILE_STEPS[step].replace("$WL", str(wl))
 
 
 def _counters(folder, key):
@@ -184,54 +270,79 @@ def _counters(folder, key):
     return {k: list(v.values()) for k, v in per.items()}
 
 
-def summarize(out_dir, workload_name):
+def _kernel_stats(folder, key):
+    """Rows of the kernel-stats csv under folder whose kernel name contains key."""
+    stats = glob.glob(os.path.join(folder, "**", "*kernel_stats.csv"), recursive=True)
+    if not stats:
+        return []
+    with open(stats[0]) as fh:
+        return [row for row in csv.DictReader(fh) if key in row["Name"]]
+
+
+def summarize(out_dir, workload_name, wl=4):
+    """Write the profiles/ summaries of workload wl (named workload_name)
+    from one profiling session's raw output; steps missing from out_dir are
+    skipped.  The traffic entry is merged into TRAFFIC_FILE under the
+    workload's name."""
+    from io_aware_softmax_fwd_amd import workloads as W
     prof = os.path.join(ROOT, "profiles")
     os.makedirs(prof, exist_ok=True)
     src_hash = kernel_source_hash()
-    lines = []
-    # kernel trace
-    stats = glob.glob(os.path.join(out_dir, "trace", "**", "*kernel_stats.csv"), recursive=True)
     avg_ns = None
-    with open(stats[0]) as fh:
-        for row in csv.DictReader(fh):
-            if KERNEL_KEY in row["Name"]:
+    rows = _kernel_stats(os.path.join(out_dir, "trace"), KERNEL_KEY)
+    if rows:
+        lines = []
+        for row in rows:
+            if avg_ns is None:
                 avg_ns = float(row["AverageNs"])
-                lines.append("kernel: %s" % row["Name"])
-                lines.append("calls=%s  average=%.1f us  min=%.1f us  max=%.1f us" % (
-                    row["Calls"], float(row["AverageNs"]) / 1e3, float(row["MinNs"]) / 1e3,
-                    float(row["MaxNs"]) / 1e3))
-    with open(os.path.join(prof, "fa_fwd_bf16_%s_kernel_trace.txt" % workload_name), "w") as f:
-        f.write("# rocprofv3 kernel trace, workload %s (kernel source %s)\n" % (workload_name, src_hash))
-        f.write("# command: %s\n" % PROFILE_STEPS["trace"])
-        f.write("\n".join(lines) + "\n")
+            lines.append("kernel: %s" % row["Name"])
+            lines.append("calls=%s  average=%.1f us  min=%.1f us  max=%.1f us" % (
+                row["Calls"], float(row["AverageNs"]) / 1e3, float(row["MinNs"]) / 1e3,
+                float(row["MaxNs"]) / 1e3))
+        with open(os.path.join(prof, "fa_fwd_bf16_%s_kernel_trace.txt" % workload_name), "w") as f:
+            f.write("# rocprofv3 kernel trace, workload %s (kernel source %s)\n" % (workload_name, src_hash))
+            f.write("# command: %s\n" % profile_command("trace", wl))
+            f.write("\n".join(lines) + "\n")
     # HBM traffic, calibrated on a copy of known size
-    fetch = _counters(os.path.join(out_dir, "fetch"), KERNEL_KEY)["FETCH_SIZE"]
-    write = _counters(os.path.join(out_dir, "write"), KERNEL_KEY)["WRITE_SIZE"]
-    cf = _counters(os.path.join(out_dir, "copy_fetch"), COPY_KEY)["FETCH_SIZE"]
-    cw = _counters(os.path.join(out_dir, "copy_write"), COPY_KEY)["WRITE_SIZE"]
-    copy_bytes = 268435456
-    f_fetch = copy_bytes / (np.mean(cf) * 1024)
-    f_write = copy_bytes / (np.mean(cw) * 1024)
-    rd = float(np.mean(fetch)) * 1024 * f_fetch
-    wr = float(np.mean(write)) * 1024 * f_write
-    traffic = {"workload": workload_name, "source_hash": src_hash,
-               "fetch_kib_per_launch": float(np.mean(fetch)), "write_kib_per_launch": float(np.mean(write)),
-               "copy_calibration": {"bytes": copy_bytes, "fetch_kib": float(np.mean(cf)),
-                                    "write_kib": float(np.mean(cw)), "fetch_factor": f_fetch,
-                                    "write_factor": f_write},
-               "read_bytes_per_launch": rd, "write_bytes_per_launch": wr,
-               "bytes_per_launch": rd + wr,
-               "commands": [PROFILE_STEPS[k] for k in ("fetch", "write", "copy_fetch", "copy_write")]}
-    with open(TRAFFIC_FILE, "w") as f:
-        json.dump(traffic, f, indent=1)
+    rd = wr = None
+    fetch = _counters(os.path.join(out_dir, "fetch"), KERNEL_KEY).get("FETCH_SIZE")
+    write = _counters(os.path.join(out_dir, "write"), KERNEL_KEY).get("WRITE_SIZE")
+    if fetch and write:
+        cf = _counters(os.path.join(out_dir, "copy_fetch"), COPY_KEY)["FETCH_SIZE"]
+        cw = _counters(os.path.join(out_dir, "copy_write"), COPY_KEY)["WRITE_SIZE"]
+        copy_bytes = 268435456
+        f_fetch = copy_bytes / (np.mean(cf) * 1024)
+        f_write = copy_bytes / (np.mean(cw) * 1024)
+        rd = float(np.mean(fetch)) * 1024 * f_fetch
+        wr = float(np.mean(write)) * 1024 * f_write
+        entry = {"workload": workload_name, "source_hash": src_hash,
+                 "fetch_kib_per_launch": float(np.mean(fetch)), "write_kib_per_launch": float(np.mean(write)),
+                 "copy_calibration": {"bytes": copy_bytes, "fetch_kib": float(np.mean(cf)),
+                                      "write_kib": float(np.mean(cw)), "fetch_factor": f_fetch,
+                                      "write_factor": f_write},
+                 "read_bytes_per_launch": rd, "write_bytes_per_launch": wr,
+                 "bytes_per_launch": rd + wr,
+                 "commands": [profile_command(k, wl) for k in ("fetch", "write", "copy_fetch", "copy_write")]}
+        w = W.WORKLOADS.get(wl)
+        if w is not None and w.name == workload_name:
+            models = io_models(w)
+            entry["models_bytes_per_launch"] = models
+            entry["measured_over_model"] = {k: (rd + wr) / v for k, v in models.items() if k != "lds_bytes_M"}
+        if avg_ns:
+            entry["kernel_avg_us"] = avg_ns / 1e3
+            entry["measured_GBps"] = (rd + wr) / (avg_ns * 1e-9) / 1e9
+        table = _traffic_table()
+        table[workload_name] = entry
+        with open(TRAFFIC_FILE, "w") as f:
+            json.dump(table, f, indent=1, sort_keys=True)
     # SQ counters
-    sq_lines = []
     sq = {}
     for part in ("sq", "sq2"):
         if os.path.isdir(os.path.join(out_dir, part)):
             for k, v in _counters(os.path.join(out_dir, part), KERNEL_KEY).items():
                 sq[k] = float(np.mean(v))
     if sq:
+        sq_lines = []
         gui = sq.get("GRBM_GUI_ACTIVE", 0.0) / 8.0          # summed over 8 XCDs
         for k in sorted(sq):
             sq_lines.append("%-28s %.4g" % (k, sq[k]))
@@ -240,28 +351,27 @@ def summarize(out_dir, workload_name):
                             % (100 * sq.get("SQ_VALU_MFMA_BUSY_CYCLES", 0) / (gui * 1024)))
             sq_lines.append("derived: VALU+MFMA co-issue = SQ_VALU_MFMA_COEXEC_CYCLES / (GRBM_GUI_ACTIVE/XCD * 1024) = %.1f %%"
                             % (100 * sq.get("SQ_VALU_MFMA_COEXEC_CYCLES", 0) / (gui * 1024)))
+        if sq.get("SQ_INSTS_MFMA"):
+            sq_lines.append("derived: non-MFMA VALU instructions per MFMA = (SQ_INSTS_VALU - SQ_INSTS_MFMA) / SQ_INSTS_MFMA = %.2f"
+                            % ((sq.get("SQ_INSTS_VALU", 0) - sq["SQ_INSTS_MFMA"]) / sq["SQ_INSTS_MFMA"]))
         with open(os.path.join(prof, "fa_fwd_bf16_%s_counters.txt" % workload_name), "w") as f:
             f.write("# rocprofv3 counters per launch, workload %s (kernel source %s)\n" % (workload_name, src_hash))
-            f.write("# commands:\n#   %s\n#   %s\n" % (PROFILE_STEPS["sq"], PROFILE_STEPS["sq2"]))
+            f.write("# commands:\n#   %s\n#   %s\n" % (profile_command("sq", wl), profile_command("sq2", wl)))
             f.write("\n".join(sq_lines) + "\n")
     # kernel-only traces of other calls (every kernel of the call)
     for step, name in TRACE_ONLY.items():
-        st = glob.glob(os.path.join(out_dir, step, "**", "*kernel_stats.csv"), recursive=True)
+        st = _kernel_stats(os.path.join(out_dir, step), "fa::")
         if not st:
             continue
-        out = []
-        with open(st[0]) as fh:
-            for row in csv.DictReader(fh):
-                if "fa::" in row["Name"]:
-                    out.append("kernel: %s\ncalls=%s  average=%.2f us  min=%.2f us  max=%.2f us" % (
-                        row["Name"], row["Calls"], float(row["AverageNs"]) / 1e3,
-                        float(row["MinNs"]) / 1e3, float(row["MaxNs"]) / 1e3))
+        out = ["kernel: %s\ncalls=%s  average=%.2f us  min=%.2f us  max=%.2f us" % (
+            row["Name"], row["Calls"], float(row["AverageNs"]) / 1e3,
+            float(row["MinNs"]) / 1e3, float(row["MaxNs"]) / 1e3) for row in st]
         with open(os.path.join(prof, "%s_kernel_trace.txt" % name), "w") as f:
             f.write("# rocprofv3 kernel trace, %s (kernel source %s)\n" % (name, src_hash))
             f.write("# command: %s\n" % PROFILE_STEPS[step])
             f.write("\n".join(out) + "\n")
     print(json.dumps({"kernel_avg_us": avg_ns / 1e3 if avg_ns else None,
-                      "traffic_bytes": rd + wr, "read": rd, "write": wr}))
+                      "traffic_bytes": (rd + wr) if rd is not None else None, "read": rd, "write": wr}))
 
 
 def decode_bench(fa, args):
@@ -289,9 +399,12 @@ def decode_bench(fa, args):
     ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr())
     tail = (1, nk, d, scale, 1, splits, ws.data_ptr(), ws.numel(), stream.cuda_stream)
     a = ptrs + ((B, H, hkv) if args.hkv else (B, H)) + tail
-    for _ in range(args.warmup):
-        assert f(*a) == 0
-    torch.cuda.synchronize()
+    def step():
+        st = f(*a)
+        if st != 0:
+            raise fa.FaError(st, f.__name__)
+
+    settled = run_untimed(step, torch.cuda.synchronize, args.warmup, args.settle_ms)
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     ev0.record(stream)
     for _ in range(args.steps):
@@ -303,6 +416,7 @@ def decode_bench(fa, args):
     print(json.dumps({"metric": "decode K/V read GB/s (1 query row, causal, %s)" % f.__name__,
                       "value": round(kv_bytes / (ms * 1e-3) / 1e9, 1), "unit": "GB/s",
                       "ms_per_step": round(ms, 4), "steps": args.steps, "warmup": args.warmup,
+                      "settle": {"ms": args.settle_ms, "steps": settled},
                       "config": {"workload": "decode", "B": B, "H": H, "Hkv": hkv, "Nq": 1,
                                  "Nk": nk, "d": d, "splits": splits},
                       "peak_hbm_GBps": 8000}), flush=True)
@@ -334,11 +448,13 @@ def bwd_bench(fa, args, w, x):
           dq.data_ptr(), dk.data_ptr(), dv.data_ptr()) + heads +
          (w.N, w.d, w.scale, int(w.causal), ws.data_ptr(), ws.numel(), stream.cuda_stream))
     call = fa.fa_bwd_gqa if args.hkv else fa.fa_bwd
-    for _ in range(args.warmup):
+
+    def step():
         st = call(*a)
         if st != 0:
             raise fa.FaError(st, call.__name__)
-    torch.cuda.synchronize()
+
+    settled = run_untimed(step, torch.cuda.synchronize, args.warmup, args.settle_ms)
     for t in (dq, dk, dv):
         if not torch.isfinite(t.float()).all():
             raise RuntimeError("non-finite gradient")
@@ -355,6 +471,7 @@ def bwd_bench(fa, args, w, x):
     return {"metric": "attention backward TFLOP/s (2.5x forward FLOPs: 5 N^2 d products, causal halved)",
             "value": round(flops / (wall / args.steps) / 1e12, 2), "unit": "TFLOP/s", "n_gpus": 1,
             "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall * 1e3 / args.steps, 4),
+            "settle": {"ms": args.settle_ms, "steps": settled}, "gpu_state": gpu_state(),
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
             "data": "synthetic (seeded N(0,1) draws, bf16-rounded)",
             "config": {"workload": w.name + "_bwd" + ("_hkv%d" % hkv if args.hkv else ""), "B": w.B,
@@ -394,11 +511,13 @@ def fp8_bench(fa, args, w, x):
     a = ((q8.data_ptr(), qs.data_ptr(), k8.data_ptr(), ks.data_ptr(), v8t.data_ptr(), vs.data_ptr(),
           o.data_ptr(), lse.data_ptr()) + heads + (w.N, w.d, w.scale, int(w.causal), stream.cuda_stream))
     call = fa.fa_fwd_fp8_gqa if args.hkv else fa.fa_fwd_fp8
-    for _ in range(args.warmup):
+
+    def step():
         st = call(*a)
         if st != 0:
             raise fa.FaError(st, call.__name__)
-    torch.cuda.synchronize()
+
+    settled = run_untimed(step, torch.cuda.synchronize, args.warmup, args.settle_ms)
     if not (torch.isfinite(lse).all() and torch.isfinite(o.float()).all()):
         raise RuntimeError("non-finite output")
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -414,6 +533,7 @@ def fp8_bench(fa, args, w, x):
     return {"metric": "fp8 fwd attention TFLOP/s (4BHN^2d, causal halved), MX E4M3 inputs resident",
             "value": round(w.flops / (wall / args.steps) / 1e12, 2), "unit": "TFLOP/s", "n_gpus": 1,
             "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall * 1e3 / args.steps, 4),
+            "settle": {"ms": args.settle_ms, "steps": settled}, "gpu_state": gpu_state(),
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp8_e4m3",
             "data": "synthetic (seeded N(0,1) draws, bf16-rounded, then MX E4M3 block-quantized)",
             "config": {"workload": w.name + "_fp8" + ("_hkv%d" % hkv if args.hkv else ""), "B": w.B,
@@ -439,11 +559,14 @@ def main():
     ap.add_argument("--hkv", type=int, default=0, metavar="HKV")
     ap.add_argument("--bwd", action="store_true")
     ap.add_argument("--fp8", action="store_true")
+    ap.add_argument("--settle-ms", type=float, default=1500.0,
+                    help="keep running untimed steps after the warm-up until this much wall time "
+                         "has passed since the first warm-up step (0: off)")
     args = ap.parse_args()
 
     if args.summarize:
         from io_aware_softmax_fwd_amd import workloads as W
-        summarize(args.summarize, W.WORKLOADS[args.workload].name)
+        summarize(args.summarize, W.WORKLOADS[args.workload].name, args.workload)
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -527,9 +650,7 @@ def main():
         if st != 0:
             raise fa.FaError(st, f.__name__)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    settled = run_untimed(step, torch.cuda.synchronize, args.warmup, args.settle_ms)
     if not (torch.isfinite(lse).all() and torch.isfinite(o.float()).all()):
         raise RuntimeError("non-finite output")
 
@@ -544,6 +665,7 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     kernel_ms = ev0.elapsed_time(ev1) / args.steps
+    state = gpu_state()
 
     ms_per_step = wall * 1e3 / args.steps
     value = w.flops / (ms_per_step * 1e-3) / 1e12
@@ -552,6 +674,19 @@ def main():
     n_rows = w.B * w.H * w.N
     alg_bytes = (w.algorithmic_bytes if not args.hkv else
                  2 * n_rows * w.d * 2 + 2 * w.B * hkv * w.N * w.d * 2 + 4 * n_rows)
+    # C1 (fp32) runs on the vector ALUs: its roof is the fp32 vector peak
+    bound, peak = ("mfma", PEAK_BF16_TFLOPS) if w.dtype == "bf16" else ("alu", PEAK_FP32_VECTOR_TFLOPS)
+    roof = {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+            "frac": round(achieved / peak, 4), "traffic": traffic, "kernel_ms": round(kernel_ms, 4),
+            "algorithmic_bytes": alg_bytes}
+    if state and state.get("gfx_clock_mhz_mean"):
+        # the same fraction against the peak scaled to the clock the run had
+        roof["frac_at_measured_clock"] = round(achieved / (peak * state["gfx_clock_mhz_mean"] / PEAK_CLOCK_MHZ), 4)
+    hbm = {"algorithmic_bytes": alg_bytes,
+           "algorithmic_GBps": round(alg_bytes / (kernel_ms * 1e-3) / 1e9, 1),
+           "measured_bytes": traffic,
+           "measured_GBps": round(traffic / (kernel_ms * 1e-3) / 1e9, 1) if traffic else None,
+           "peak_GBps": PEAK_HBM_GBPS}
     line = {
         "metric": "fwd attention TFLOP/s (4BHN^2d, causal halved) + % bf16 MFMA peak, N=16K d=128",
         "value": round(value, 2),
@@ -559,6 +694,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle": {"ms": args.settle_ms, "steps": settled},
         "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -569,10 +705,9 @@ def main():
         "config": {"workload": w.name + ("_hkv%d" % hkv if args.hkv else ""), "B": w.B, "H": w.H,
                    "Hkv": hkv, "N": w.N, "d": w.d, "causal": w.causal,
                    "amplified_rows": w.amplify, "flops": w.flops, "entry_point": f.__name__},
-        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": traffic, "kernel_ms": round(kernel_ms, 4),
-                     "algorithmic_bytes": alg_bytes},
+        "roofline": roof,
+        "hbm": hbm,
+        "gpu_state": state,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

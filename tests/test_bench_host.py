@@ -62,7 +62,7 @@ def session(tmp_path, monkeypatch):
 def test_summary_scales_counters_by_the_copy(session, capsys):
     tmp, out = session
     bench.summarize(out, "wl")
-    t = json.load(open(str(tmp / "profiles" / "traffic.json")))
+    t = json.load(open(str(tmp / "profiles" / "traffic.json")))["wl"]
     cal = t["copy_calibration"]
     assert cal["fetch_factor"] == pytest.approx(2.0) and cal["write_factor"] == pytest.approx(1.0)
     assert t["fetch_kib_per_launch"] == pytest.approx(810000.0)
@@ -82,3 +82,40 @@ def test_traffic_reported_only_for_the_same_source_and_workload(session, monkeyp
     assert bench.measured_traffic("other") is None
     monkeypatch.setattr(bench, "kernel_source_hash", lambda: "fedcba9876543210")
     assert bench.measured_traffic("wl") is None
+
+
+def test_summary_keeps_other_workloads(session):
+    tmp, out = session
+    bench.summarize(out, "wl")
+    bench.summarize(out, "wl2")
+    t = json.load(open(str(tmp / "profiles" / "traffic.json")))
+    assert set(t) == {"wl", "wl2"}
+    assert bench.measured_traffic("wl2") == pytest.approx(bench.measured_traffic("wl"))
+
+
+def test_io_models_match_the_pages_formulas():
+    """Per head: 4N^2 + 4Nd elements for the three-pass attention and
+    8 N^2 d^2 / M for the tiled pass (M elements of on-chip memory)."""
+    from io_aware_softmax_fwd_amd import workloads as W
+    w = W.WORKLOADS[4]
+    m = bench.io_models(w)
+    N, d, heads = 16384, 128, 32
+    assert m["algorithmic"] == heads * (4 * N * d * 2 + 4 * N)
+    assert m["standard_4N2_4Nd"] == heads * (4 * N * N + 4 * N * d) * 2
+    assert m["tiled_8N2d2_over_M"] == pytest.approx(heads * 8 * N * N * d * d / (160 * 1024 / 2) * 2)
+    # causal: query tile t reads keys [0, 128 (t+1)) of K and of V
+    kv = sum(128 * (t + 1) for t in range(N // 128))
+    assert m["kv_per_query_tile"] == heads * (2 * kv * d * 2 + 2 * N * d * 2 + 4 * N)
+    w2 = W.WORKLOADS[5]
+    m2 = bench.io_models(w2)
+    tiles = -(-32749 // 128)
+    assert m2["kv_per_query_tile"] == 16 * (2 * tiles * 32749 * 64 * 2 + 2 * 32749 * 64 * 2 + 4 * 32749)
+
+
+def test_untimed_steps_run_warmup_then_settle():
+    calls = []
+    n = bench.run_untimed(lambda: calls.append(1), lambda: None, 3, 0.0)
+    assert n == 0 and len(calls) == 3
+    calls.clear()
+    n = bench.run_untimed(lambda: calls.append(1), lambda: None, 2, 20.0)
+    assert n > 0 and n % 8 == 0 and len(calls) == 2 + n
