@@ -52,7 +52,8 @@ enum fa_status {
   FA_ERR_ALIAS = 8,          /* an output or the workspace overlaps a buffer   */
   FA_ERR_WORKSPACE = 9,      /* workspace NULL or smaller than required        */
   FA_ERR_SPLITS = 10,        /* num_splits outside 1..256                      */
-  FA_ERR_HEADS = 11          /* H is not a multiple of Hkv                     */
+  FA_ERR_HEADS = 11,         /* H is not a multiple of Hkv                     */
+  FA_ERR_SCRATCH = 12        /* key-split partials exceed the static scratch   */
 };
 
 /*
@@ -125,6 +126,34 @@ size_t fa_fwd_splitkv_workspace_size(int B, int H, int Nq, int d, int num_splits
  * two per CU with chunks of at least 4 tiles; else one per CU with chunks of
  * 8 tiles, or of 4 when the keys are fewer.  Host only, no HIP call. */
 int fa_fwd_splitkv_num_splits(int B, int H, int Nq, int Nk, int num_cus);
+
+/*
+ * fa_fwd_splitkv without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc).  The call allocates nothing: the
+ * fp32 key-split partials go to a static device array owned by the library,
+ * fa_fwd_splitkv_noalloc_max_bytes() bytes (32 MiB) on each GPU the library
+ * has been loaded on, held until the process ends.  Its device address is
+ * looked up once per GPU (on the first call for that GPU, with the stream's
+ * GPU made current for the lookup) and cached.
+ *   Arguments, layout and results as for fa_fwd_splitkv with the same
+ *   num_splits (the same kernels run, so the outputs are bit-identical).
+ *   Errors as for fa_fwd_splitkv, except that FA_ERR_WORKSPACE cannot occur;
+ *   FA_ERR_SCRATCH when fa_fwd_splitkv_workspace_size(B, H, Nq, d,
+ *   num_splits) exceeds fa_fwd_splitkv_noalloc_max_bytes() (checked on the
+ *   host before any HIP call); FA_ERR_HIP if the scratch lookup or a launch
+ *   fails.
+ * Every call on one GPU shares that GPU's scratch and nothing in it is kept
+ * from one call to the next (every partial is written before it is read):
+ * calls that overlap in time on one GPU (two streams, or two host threads)
+ * race on it and must be serialised by the caller.
+ */
+int fa_fwd_splitkv_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                           int B, int H, int Nq, int Nk, int d, float scale, int causal,
+                           int num_splits, hipStream_t stream);
+
+/* Size in bytes of the static scratch of fa_fwd_splitkv_noalloc.  Host only. */
+size_t fa_fwd_splitkv_noalloc_max_bytes(void);
 
 /*
  * Attention forward with grouped K/V heads (bf16): multi-query and

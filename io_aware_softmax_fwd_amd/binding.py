@@ -11,6 +11,9 @@ Low level (same names and arguments as the C functions, raw pointers):
                    num_splits, workspace, workspace_bytes, stream) -> status
     fa_fwd_splitkv_workspace_size(B, H, Nq, d, num_splits)     -> bytes
     fa_fwd_splitkv_num_splits(B, H, Nq, Nk, num_cus)           -> count
+    fa_fwd_splitkv_noalloc(q, k, v, o, lse, B, H, Nq, Nk, d, scale,
+                           causal, num_splits, stream)         -> status
+    fa_fwd_splitkv_noalloc_max_bytes()                         -> bytes
     fa_fwd_gqa(q, k, v, o, lse, B, H, Hkv, Nq, Nk, d, scale, causal,
                num_splits, workspace, workspace_bytes, stream) -> status
     fa_fwd_gqa_num_splits(B, H, Hkv, Nq, Nk, causal, num_cus)  -> count
@@ -63,9 +66,11 @@ FA_ERR_ALIAS = 8
 FA_ERR_WORKSPACE = 9
 FA_ERR_SPLITS = 10
 FA_ERR_HEADS = 11
+FA_ERR_SCRATCH = 12
 
 EXPORTED = ("fa_fwd", "fa_fwd_f32", "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_size",
-            "fa_fwd_splitkv_num_splits", "fa_fwd_gqa", "fa_fwd_gqa_num_splits", "fa_bwd",
+            "fa_fwd_splitkv_num_splits", "fa_fwd_splitkv_noalloc", "fa_fwd_splitkv_noalloc_max_bytes",
+            "fa_fwd_gqa", "fa_fwd_gqa_num_splits", "fa_bwd",
             "fa_bwd_workspace_size", "fa_bwd_gqa", "fa_bwd_gqa_workspace_size", "fa_quantize_qk_fp8", "fa_quantize_v_fp8", "fa_fp8_v_bytes",
             "fa_fp8_v_scale_bytes", "fa_fwd_fp8", "fa_fwd_fp8_gqa", "fa_strerror")
 
@@ -128,6 +133,11 @@ def load():
     lib.fa_fwd_splitkv_workspace_size.argtypes = [ctypes.c_int] * 5
     lib.fa_fwd_splitkv_num_splits.restype = ctypes.c_int
     lib.fa_fwd_splitkv_num_splits.argtypes = [ctypes.c_int] * 5
+    lib.fa_fwd_splitkv_noalloc.restype = ctypes.c_int
+    lib.fa_fwd_splitkv_noalloc.argtypes = ([ctypes.c_void_p] * 5 + [ctypes.c_int] * 5 +
+                                           [ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_void_p])
+    lib.fa_fwd_splitkv_noalloc_max_bytes.restype = ctypes.c_size_t
+    lib.fa_fwd_splitkv_noalloc_max_bytes.argtypes = []
     lib.fa_fwd_gqa.restype = ctypes.c_int
     lib.fa_fwd_gqa.argtypes = ([ctypes.c_void_p] * 5 + [ctypes.c_int] * 6 +
                                [ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
@@ -188,6 +198,15 @@ def fa_fwd_splitkv_workspace_size(B, H, Nq, d, num_splits):
 
 def fa_fwd_splitkv_num_splits(B, H, Nq, Nk, num_cus):
     return int(load().fa_fwd_splitkv_num_splits(B, H, Nq, Nk, num_cus))
+
+
+def fa_fwd_splitkv_noalloc(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, num_splits, stream):
+    return load().fa_fwd_splitkv_noalloc(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, num_splits,
+                                         stream)
+
+
+def fa_fwd_splitkv_noalloc_max_bytes():
+    return int(load().fa_fwd_splitkv_noalloc_max_bytes())
 
 
 def fa_fwd_gqa(q, k, v, o, lse, B, H, Hkv, Nq, Nk, d, scale, causal, num_splits, workspace,

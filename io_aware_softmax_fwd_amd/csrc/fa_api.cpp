@@ -57,10 +57,11 @@ int validate(const void* q, const void* k, const void* v, const void* o, const f
 }
 
 // Checks of the general bf16 call (grouped K/V heads, Nq != Nk, key
-// splits).  A workspace is required only when splits > 1.
+// splits).  A workspace is required only when splits > 1 and need_ws is set
+// (the allocation-free call brings its own).
 int validate_gqa(const void* q, const void* k, const void* v, const void* o, const float* lse,
                  int B, int H, int Hkv, int Nq, int Nk, int d, float scale, int causal, int splits,
-                 const void* ws, size_t ws_bytes) {
+                 const void* ws, size_t ws_bytes, bool need_ws = true) {
   if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
   if (B < 1 || H < 1 || Hkv < 1 || Nq < 1 || Nk < 1) return FA_ERR_SHAPE;
   if (H % Hkv != 0) return FA_ERR_HEADS;
@@ -87,7 +88,7 @@ int validate_gqa(const void* q, const void* k, const void* v, const void* o, con
       overlap(lse, lb, q, qb) || overlap(lse, lb, k, kb) || overlap(lse, lb, v, kb) ||
       overlap(lse, lb, o, qb))
     return FA_ERR_ALIAS;
-  if (splits > 1) {
+  if (splits > 1 && need_ws) {
     const fa::SplitLayout L = fa::splitkv_layout(B, H, Nq, d, splits);
     if (!ws || (int64_t)ws_bytes < L.total) return FA_ERR_WORKSPACE;
     if (misaligned(ws)) return FA_ERR_ALIGN;
@@ -213,6 +214,21 @@ int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* 
   return fa::launch_fwd_bf16(p, stream) == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
+size_t fa_fwd_splitkv_noalloc_max_bytes(void) { return (size_t)fa::kNoAllocScratchBytes; }
+
+int fa_fwd_splitkv_noalloc(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                           int H, int Nq, int Nk, int d, float scale, int causal, int num_splits,
+                           hipStream_t stream) {
+  const int st = validate_gqa(q, k, v, o, lse, B, H, H, Nq, Nk, d, scale, causal, num_splits,
+                              nullptr, 0, false);
+  if (st != FA_OK) return st;
+  if (fa::splitkv_layout(B, H, Nq, d, num_splits).total > fa::kNoAllocScratchBytes) return FA_ERR_SCRATCH;
+  void* scratch = nullptr;
+  if (fa::noalloc_scratch(stream, &scratch) != hipSuccess) return FA_ERR_HIP;
+  const fa::GqaProblem p{q, k, v, o, lse, B, H, H, Nq, Nk, d, scale, causal, num_splits, scratch};
+  return fa::launch_fwd_bf16(p, stream) == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 int fa_fwd_gqa_num_splits(int B, int H, int Hkv, int Nq, int Nk, int causal, int num_cus) {
   return choose_splits(B, H, Hkv, Nq, Nk, causal, num_cus);
 }
@@ -332,6 +348,7 @@ const char* fa_strerror(int status) {
     case FA_ERR_WORKSPACE: return "workspace missing or smaller than the size query returns";
     case FA_ERR_SPLITS: return "num_splits must be between 1 and 256";
     case FA_ERR_HEADS: return "H must be a multiple of Hkv";
+    case FA_ERR_SCRATCH: return "the key-split partials exceed the static scratch (fa_fwd_splitkv_noalloc_max_bytes); use fa_fwd_splitkv with a workspace";
     default: return "unknown status";
   }
 }

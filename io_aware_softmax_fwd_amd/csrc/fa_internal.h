@@ -152,6 +152,14 @@ inline SplitLayout splitkv_layout(int B, int H, int Nq, int d, int splits) {
   return L;
 }
 
+// Bytes of the static device scratch that the allocation-free key-split call
+// uses in place of a caller's workspace (one copy per GPU).
+constexpr int64_t kNoAllocScratchBytes = int64_t(32) << 20;
+
+// Device address of that scratch on the GPU `stream` belongs to; looked up
+// once per GPU and cached.  Returns the HIP status of the lookup.
+hipError_t noalloc_scratch(hipStream_t stream, void** ptr);
+
 // Each launcher queues its kernels on `stream` and returns the HIP status of
 // the launch (hipSuccess or the runtime's error).
 hipError_t launch_fwd_f32(const Problem& p, hipStream_t stream);

@@ -342,3 +342,36 @@ def test_fwd_fp8_gqa_checks_on_host():
     assert call(k8=None) == fa.FA_ERR_NULL
     # K codes of B*Hkv*N rows (8 KB here): an output 4 KB in overlaps them
     assert call(o=A + 16 * MB + 4096) == fa.FA_ERR_ALIAS
+
+
+def _noalloc_call(**kw):
+    args = dict(q=A, k=A + 8 * MB, v=A + 16 * MB, o=A + 24 * MB, lse=A + 32 * MB,
+                B=1, H=2, Nq=64, Nk=128, d=64, scale=0.125, causal=0, splits=2, stream=None)
+    args.update(kw)
+    return fa.fa_fwd_splitkv_noalloc(args["q"], args["k"], args["v"], args["o"], args["lse"],
+                                     args["B"], args["H"], args["Nq"], args["Nk"], args["d"],
+                                     args["scale"], args["causal"], args["splits"], args["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), fa.FA_ERR_NULL), (dict(lse=None), fa.FA_ERR_NULL),
+    (dict(Nq=0), fa.FA_ERR_SHAPE), (dict(causal=1, Nq=129, Nk=128), fa.FA_ERR_SHAPE),
+    (dict(d=80), fa.FA_ERR_UNSUPPORTED_D), (dict(scale=0.0), fa.FA_ERR_SCALE),
+    (dict(causal=3), fa.FA_ERR_CAUSAL),
+    (dict(splits=0), fa.FA_ERR_SPLITS), (dict(splits=257), fa.FA_ERR_SPLITS),
+    (dict(v=A + 16 * MB + 4), fa.FA_ERR_ALIGN), (dict(o=A + 8 * MB), fa.FA_ERR_ALIAS),
+    # partials of 4 splits x 16384 rows x 128 dims x 4 B = 32 MiB, plus the
+    # LSE part: one byte too many for the 32 MiB scratch
+    (dict(B=1, H=16, Nq=1024, Nk=4096, d=128, splits=4, q=A, k=A + 64 * MB, v=A + 128 * MB,
+          o=A + 192 * MB, lse=A + 256 * MB), fa.FA_ERR_SCRATCH),
+])
+def test_noalloc_bad_arguments_rejected_on_host(kw, status):
+    assert _noalloc_call(**kw) == status
+
+
+def test_noalloc_scratch_limit():
+    cap = fa.fa_fwd_splitkv_noalloc_max_bytes()
+    assert cap == 32 << 20
+    # the largest decoding call of the test suite fits, with room to spare
+    assert fa.fa_fwd_splitkv_workspace_size(1, 32, 1, 128, 256) <= cap
+    assert fa.fa_fwd_splitkv_workspace_size(1, 16, 1024, 128, 4) > cap
