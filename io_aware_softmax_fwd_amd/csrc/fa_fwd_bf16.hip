@@ -54,6 +54,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <type_traits>
 
 #include "fa_device.h"
 #include "fa_internal.h"
@@ -198,9 +199,10 @@ struct Fwd {
 
   // Online-softmax step of one 32-row block for the tile at key k0: writes
   // the bf16 probabilities, moving the offset (and rescaling) when needed,
-  // and adds their row sum.
-  template <bool MASK>
-  __device__ void softmax(int qb, f32x16 (&s)[KB], bf16x8 (&pf)[PS], int k0) {
+  // and adds their row sum.  FIRST: the wave's first tile, whose offset is
+  // still -inf, goes straight to the row max.
+  template <bool MASK, bool FIRST = false>
+  __device__ __forceinline__ void softmax(int qb, f32x16 (&s)[KB], bf16x8 (&pf)[PS], int k0) {
     if constexpr (MASK) {
       // key = k0 + 32*kb + (r&3) + 8*(r>>2) + 4*hl must be <= min(qi+coff, N-1)
       const int lim = (CAUSAL ? min(pos[qb] + coff, N - 1) : N - 1) - k0 - 4 * hl;
@@ -215,8 +217,9 @@ struct Fwd {
     // first tile gives inf or NaN); then the offset moves to the row max
     // (wave-uniform branch; rows whose max did not rise keep alpha = 1) and
     // they are redone.
-    float ps = probs(s, pf, m[qb] * c);
-    if (__builtin_amdgcn_ballot_w64(!(ps <= kProbSumMax))) {
+    float ps = 0.f;
+    if (!FIRST) ps = probs(s, pf, m[qb] * c);
+    if (FIRST || __builtin_amdgcn_ballot_w64(!(ps <= kProbSumMax))) {
       asm volatile("" ::: "memory");
       float mx = s[0][0];
 #pragma unroll
@@ -241,14 +244,9 @@ struct Fwd {
     l[qb] += ps;
   }
 
-  // Consume the tile in buffers PAR: S^T = K Q^T for every block (each K
-  // fragment feeds all blocks), the softmax merges, then O^T += V^T P^T
-  // (each V fragment feeds all blocks).
-  template <bool MASK, int PAR>
-  __device__ void consume(int k0) {
-    const unsigned char* kt = kbuf[PAR];
-    const unsigned char* vt = vbuf[PAR];
-    f32x16 s[QB][KB];
+  // S^T = K Q^T of the tile whose K sits at kt, for every block (each K
+  // fragment feeds all blocks).
+  __device__ __forceinline__ void scores(const unsigned char* kt, f32x16 (&s)[QB][KB]) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
@@ -264,11 +262,10 @@ struct Fwd {
         for (int qb = 0; qb < QB; ++qb)
           s[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[qb][ks], s[qb][kb], 0, 0, 0);
       }
+  }
 
-    bf16x8 pf[QB][PS];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) softmax<MASK>(qb, s[qb], pf[qb], k0);
-
+  // O^T += V^T P^T with V of the tile at vt (each V fragment feeds all blocks).
+  __device__ __forceinline__ void pv(const unsigned char* vt, const bf16x8 (&pf)[QB][PS]) {
 #pragma unroll
     for (int ps = 0; ps < PS; ++ps)
 #pragma unroll
@@ -281,6 +278,18 @@ struct Fwd {
         for (int qb = 0; qb < QB; ++qb)
           acc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[qb][ps], acc[qb][db], 0, 0, 0);
       }
+  }
+
+  // Consume the tile in buffers PAR: the scores, the softmax merges, then
+  // the product with V.
+  template <bool MASK, int PAR, bool FIRST = false>
+  __device__ __forceinline__ void consume(int k0) {
+    f32x16 s[QB][KB];
+    scores(kbuf[PAR], s);
+    bf16x8 pf[QB][PS];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) softmax<MASK, FIRST>(qb, s[qb], pf[qb], k0);
+    pv(vbuf[PAR], pf);
   }
 
   // One pipeline step: queue tile j+1 into the other buffers (it gets the
@@ -476,6 +485,248 @@ __global__ __launch_bounds__(kThreads, (QB == 1 || D == 64) ? 2 : 1) void fwd_bf
   }
 }
 
+// Small grids: one workgroup per 32 query rows, its four waves splitting
+// the keys.  When ceil(rows/128) workgroups of the kernel above would leave
+// most CUs idle (a few heads of short sequences), the time is one
+// workgroup's serial walk over all key tiles.  Here every wave holds the
+// same 32 rows and takes every fourth key tile (wave w: tiles w, w+4, ...)
+// through LDS slots of its own, so a row's keys are covered by four
+// independent online-softmax passes that run side by side; the four partial
+// results (offset m, sum l and unnormalised O of each wave) then meet in LDS
+// and are merged as chunks are (LSE = log sum_w exp(LSE_w); notes page,
+// sections 5 and 12.1), each wave writing a quarter of the head dims.
+// A wave's K slot is refilled with its next tile's keys as soon as the
+// scores have read it, and the V slot once the product with V has, so each
+// load overlaps the other half of the tile's work.  A wave's first tile goes
+// straight to the row max (its offset is still -inf), and the workgroups of
+// a head first touch one share each of the head's K and V lines, so that
+// later tiles come from L2.
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void fwd_bf16_ws_kernel(
+    const unsigned short* __restrict__ q, const unsigned short* __restrict__ k,
+    const unsigned short* __restrict__ v, unsigned short* __restrict__ o,
+    float* __restrict__ lse, int Nq, int Nk, int G, int BHkv, int n_qtiles, int tph,
+    float scale, int hg) {
+  // per wave: one K and one V tile (separate arrays, so that the compiler
+  // sees that V loads in flight do not touch K and the other way round)
+  __shared__ __attribute__((aligned(1024))) unsigned char k_lds[kWaves][Cfg<D>::kTile];
+  __shared__ __attribute__((aligned(1024))) unsigned char v_lds[kWaves][Cfg<D>::vTile];
+  constexpr int KS = D / 16, DB = D / 32, BR = 32;
+  constexpr int kDma = Cfg<D>::kDma, vDma = Cfg<D>::vDma;
+  using F = Fwd<D, 1, CAUSAL, true>;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  int bkv, idx;
+  xcd_order(blockIdx.x, BHkv, n_qtiles, hg, bkv, idx);
+  const int R = G * Nq;
+  int r0, nr;
+  if (tph == 0) {
+    r0 = (n_qtiles - 1 - idx) * BR;
+    nr = min(BR, R - r0);
+  } else {
+    const int pt = tph - 1 - idx / G;
+    r0 = (idx % G) * Nq + pt * BR;
+    nr = min(BR, Nq - pt * BR);
+  }
+  const int64_t qblock = (int64_t)bkv * R;
+  const int64_t khead = (int64_t)bkv * Nk * D;
+
+  F f;
+  unsigned char* const kt = k_lds[wave];
+  unsigned char* const vt = v_lds[wave];
+  f.kh = k + khead;
+  f.vh = v + khead;
+  f.N = Nk;
+  f.coff = Nk - Nq;
+  f.wave = wave;
+  f.l32 = lane & 31;
+  f.hl = lane >> 5;
+  f.rows = true;
+  int pmin, pmax;
+  position_range(r0, nr, Nq, pmin, pmax);
+  f.wlast = pmax + f.coff;
+  f.c = scale * kLog2e;
+  f.m[0] = -INFINITY;
+  f.l[0] = 0.f;
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) f.acc[0][db][r] = 0.f;
+  f.pos[0] = (r0 + f.l32) % Nq;
+  {
+    const unsigned short* qrow = q + (qblock + r0 + f.l32) * D;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      u32x4 raw = {0u, 0u, 0u, 0u};
+      if (f.l32 < nr) raw = *reinterpret_cast<const u32x4*>(qrow + 16 * ks + 8 * f.hl);
+      f.qf[0][ks] = __builtin_bit_cast(bf16x8, raw);
+    }
+  }
+  f.setup_offsets(lane);   // fragment read offsets (its DMA slots are not used)
+  // this wave loads whole tiles: LDS-DMA block i covers 16-byte slots
+  // 64 i .. 64 i + 63 of the tile
+  int koff[kDma], voff[vDma];
+#pragma unroll
+  for (int i = 0; i < kDma; ++i) {
+    const int slot = i * 64 + lane;
+    const int r = slot / Cfg<D>::CH, pc = slot % Cfg<D>::CH;
+    koff[i] = r * (2 * D) + 16 * (pc ^ Cfg<D>::kswz(r));
+  }
+#pragma unroll
+  for (int i = 0; i < vDma; ++i) {
+    const int slot = i * 64 + lane;
+    const int r = slot / Cfg<D>::CH, pc = slot % Cfg<D>::CH;
+    voff[i] = r * (2 * D) + 16 * (pc ^ Cfg<D>::vswz(r));
+  }
+  auto load_k = [&](int k0) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    const __amdgpu_buffer_rsrc_t rs = tile_rsrc<D>(f.kh, k0, Nk);
+#pragma unroll
+    for (int i = 0; i < kDma; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(kt + i * 1024), 16, koff[i], 0, 0, 0);
+#endif
+  };
+  auto load_v = [&](int k0) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    const __amdgpu_buffer_rsrc_t rs = tile_rsrc<D>(f.vh, k0, Nk);
+#pragma unroll
+    for (int i = 0; i < vDma; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(vt + i * 1024), 16, voff[i], 0, 0, 0);
+#endif
+  };
+
+  const int kv_end = CAUSAL ? min(Nk, pmax + 1 + f.coff) : Nk;
+  const int n_tiles = (kv_end + kKeys - 1) / kKeys;
+  const int n_full = CAUSAL ? min(pmin + f.coff + 1, Nk) / kKeys : Nk / kKeys;
+
+  // One tile: its K and V were queued (K first); refill each slot with the
+  // next tile's keys once it has been read.  Loads return in order, so
+  // waiting until at most vDma (kDma) loads are outstanding means that the
+  // K (V) loads issued before them have landed.
+  auto tile = [&](auto mask, auto first, int j) {
+    constexpr bool MASK = decltype(mask)::value;
+    constexpr bool FIRST = decltype(first)::value;
+    const int jn = j + kWaves;
+    const bool more = jn < n_tiles;
+    f32x16 s[1][F::KB];
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(vDma) : "memory");
+    f.scores(kt, s);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    if (more) load_k(jn * kKeys);
+    bf16x8 pf[1][F::PS];
+    f.template softmax<MASK, FIRST>(0, s[0], pf[0], j * kKeys);
+    if (more) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kDma) : "memory");
+    else      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    f.pv(vt, pf);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    if (more) load_v(jn * kKeys);
+  };
+  constexpr int kPrefetch = 2;
+  unsigned warm[kPrefetch];
+  {
+    const int64_t lines = ((int64_t)kv_end * 2 * D + 127) / 128;    // per tensor
+    const int64_t per = (lines + n_qtiles - 1) / n_qtiles;
+    const __amdgpu_buffer_rsrc_t rk = tile_rsrc<D>(f.kh, 0, Nk);
+    const __amdgpu_buffer_rsrc_t rv = tile_rsrc<D>(f.vh, 0, Nk);
+#pragma unroll
+    for (int i = 0; i < kPrefetch; ++i) {
+      const int64_t e = (int64_t)i * kThreads + tid;
+      const int64_t line = (int64_t)idx * per + (e % per);
+      warm[i] = 0u;
+      if (e < 2 * per && line < lines)
+        warm[i] = __builtin_amdgcn_raw_buffer_load_b32(e < per ? rk : rv, (int)(line * 128), 0, 0);
+    }
+  }
+  int j = wave;
+  if (j < n_tiles) {
+    load_k(j * kKeys);
+    load_v(j * kKeys);
+    if (j >= n_full) tile(std::true_type{}, std::true_type{}, j);
+    else             tile(std::false_type{}, std::true_type{}, j);
+    j += kWaves;
+    for (; j < min(n_full, n_tiles); j += kWaves) tile(std::false_type{}, std::false_type{}, j);
+    for (; j < n_tiles; j += kWaves) tile(std::true_type{}, std::false_type{}, j);
+  }
+  {
+    unsigned x = 0u;
+#pragma unroll
+    for (int i = 0; i < kPrefetch; ++i) x ^= warm[i];
+    asm volatile("" ::"v"(x));
+  }
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+  __syncthreads();
+
+  // Partial results to LDS: the unnormalised O^T of the wave as fp32
+  // [32 rows][D] in its K slot (16-byte chunk c of row r at c ^ (r % 16)),
+  // its offsets and row sums in its V slot.
+  const float l_tot = sum_across_halves(f.l[0]);
+  {
+    float* ob = reinterpret_cast<float*>(kt);
+    float* ml = reinterpret_cast<float*>(vt);
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int c = 8 * db + 2 * g + f.hl;    // chunk of dims 32 db + 8 g + 4 hl
+        const float4 w = {f.acc[0][db][4 * g], f.acc[0][db][4 * g + 1], f.acc[0][db][4 * g + 2],
+                          f.acc[0][db][4 * g + 3]};
+        *reinterpret_cast<float4*>(ob + f.l32 * D + 4 * (c ^ (f.l32 & 15))) = w;
+      }
+    if (f.hl == 0) {
+      ml[f.l32] = f.m[0];
+      ml[32 + f.l32] = l_tot;
+    }
+  }
+  __syncthreads();
+
+  // Merge: wave w writes head dims [w D/4, (w+1) D/4) of the 32 rows; lane
+  // (row, half) takes D/8 of them.  Key 0 is visible to every row and sits
+  // in wave 0's first tile, so the row max M is finite; a wave that saw no
+  // key of a row (offset -inf) weighs 0.
+  const int row = lane & 31, hh = lane >> 5;
+  constexpr int NC = D / 32;                   // 16-byte chunks per lane
+  float mw[kWaves], M = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    mw[w] = reinterpret_cast<const float*>(v_lds[w])[row];
+    M = fmaxf(M, mw[w]);
+  }
+  float L = 0.f;
+  float out[4 * NC];
+#pragma unroll
+  for (int e = 0; e < 4 * NC; ++e) out[e] = 0.f;
+  const int c0 = wave * (D / 16) + hh * NC;   // first chunk of this lane
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    const float a = mw[w] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((mw[w] - M) * f.c);
+    L += a * reinterpret_cast<const float*>(v_lds[w])[32 + row];
+    const float* ob = reinterpret_cast<const float*>(k_lds[w]);
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const float4 x = *reinterpret_cast<const float4*>(ob + row * D + 4 * ((c0 + c) ^ (row & 15)));
+      out[4 * c] += a * x.x;
+      out[4 * c + 1] += a * x.y;
+      out[4 * c + 2] += a * x.z;
+      out[4 * c + 3] += a * x.w;
+    }
+  }
+  if (row >= nr) return;
+  const int64_t grow = qblock + r0 + row;
+  const float inv = 1.f / L;
+  unsigned short* orow = o + grow * D + 4 * c0;
+#pragma unroll
+  for (int c = 0; c < NC; c += 2) {
+    const u32x4 w = {pack_bf16x2(out[4 * c] * inv, out[4 * c + 1] * inv),
+                     pack_bf16x2(out[4 * c + 2] * inv, out[4 * c + 3] * inv),
+                     pack_bf16x2(out[4 * c + 4] * inv, out[4 * c + 5] * inv),
+                     pack_bf16x2(out[4 * c + 6] * inv, out[4 * c + 7] * inv)};
+    *reinterpret_cast<u32x4*>(orow + 4 * c) = w;
+  }
+  if (wave == 0 && hh == 0) lse[grow] = M * scale + logf(L);
+}
+
 // Merge of the key chunks of every row: LSE = log sum_s exp(LSE_s) and
 // O = sum_s exp(LSE_s - LSE) O_s, the online-softmax merge applied to whole
 // chunks (zzszmyf.github.io notes, sections 5 and 12.1).  One workgroup per
@@ -630,6 +881,13 @@ __global__ __launch_bounds__(256) void merge_rows_kernel(const float* __restrict
 
 // Rows above which the merge runs one thread per (row, 8 dims).
 constexpr int64_t kMergeRowsMin = 4096;
+// Up to this many 128-row workgroups (three quarters of the 256 CUs) a call
+// with at least kWsMinTiles key tiles runs fwd_bf16_ws_kernel instead:
+// 32-row workgroups whose four waves split the keys.  Measured against the
+// 128-row kernel: faster at 128 and 192 workgroups (d = 64 and 128, causal
+// or not), slower at 240 and 256 (d = 128 non-causal at 256: 62 vs 40 us).
+constexpr int64_t kWsMaxGrid = 192;
+constexpr int kWsMinTiles = 8;
 // Workgroups from which d = 64 takes 256-row tiles: two per CU of the 256.
 constexpr int64_t kWideTileMinGrid = 512;
 
@@ -661,6 +919,14 @@ hipError_t launch(const GqaProblem& p, hipStream_t stream) {
         return hipGetLastError();
       }
     }
+  }
+  if (p.splits == 1 && t.n_qtiles * BHkv <= kWsMaxGrid && (p.Nk + kKeys - 1) / kKeys >= kWsMinTiles) {
+    const QueryTiling t32 = query_tiling(G, p.Nq, p.causal, 32);
+    const dim3 grid((unsigned)(t32.n_qtiles * BHkv));
+    hipLaunchKernelGGL((fwd_bf16_ws_kernel<D, CAUSAL>), grid, block, 0, stream, q, k, v,
+                       static_cast<unsigned short*>(p.o), p.lse, p.Nq, p.Nk, G, BHkv, (int)t32.n_qtiles,
+                       t32.tph, p.scale, xcd_head_group(BHkv, t32.n_qtiles, G, t32.tph, 1));
+    return hipGetLastError();
   }
   if (p.splits == 1) {
     const dim3 grid((unsigned)(t.n_qtiles * BHkv));
