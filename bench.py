@@ -210,7 +210,7 @@ def gpu_state():
 # are the same for every workload (C4 shapes).
 PROFILE_STEPS = {
     "trace": "rocprofv3 --kernel-trace --stats --output-format csv -d $OUT/trace -o run "
-             "-- python bench.py --workload $WL --no-cpu-baseline",
+             "-- python bench.py --workload $WL --settle-ms 0 --no-cpu-baseline",
     "fetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d $OUT/fetch -o run "
              "-- python bench.py --workload $WL --steps 3 --warmup 1 --settle-ms 0 --no-cpu-baseline",
     "write": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d $OUT/write -o run "
@@ -227,6 +227,22 @@ PROFILE_STEPS = {
            "SQ_ACTIVE_INST_LDS SQ_INSTS_VALU_TRANS_F32 SQ_ACTIVE_INST_ANY GRBM_GUI_ACTIVE "
            "--output-format csv -d $OUT/sq2 -o run "
            "-- python bench.py --workload $WL --steps 3 --warmup 1 --settle-ms 0 --no-cpu-baseline",
+    "bwd_sq": "rocprofv3 --pmc SQ_WAVE_CYCLES SQ_BUSY_CYCLES SQ_VALU_MFMA_BUSY_CYCLES "
+              "SQ_VALU_MFMA_COEXEC_CYCLES SQ_ACTIVE_INST_VALU SQ_WAIT_INST_LDS SQ_WAIT_ANY "
+              "SQ_LDS_BANK_CONFLICT GRBM_GUI_ACTIVE --output-format csv -d $OUT/bwd_sq -o run "
+              "-- python bench.py --bwd --steps 3 --warmup 1 --settle-ms 0",
+    "bwd_sq2": "rocprofv3 --pmc SQ_INSTS_VALU SQ_INSTS_MFMA SQ_INSTS_LDS SQ_INSTS_SALU "
+               "SQ_ACTIVE_INST_LDS SQ_INSTS_VALU_TRANS_F32 SQ_ACTIVE_INST_ANY GRBM_GUI_ACTIVE "
+               "--output-format csv -d $OUT/bwd_sq2 -o run "
+               "-- python bench.py --bwd --steps 3 --warmup 1 --settle-ms 0",
+    "fp8_sq": "rocprofv3 --pmc SQ_WAVE_CYCLES SQ_BUSY_CYCLES SQ_VALU_MFMA_BUSY_CYCLES "
+              "SQ_VALU_MFMA_COEXEC_CYCLES SQ_ACTIVE_INST_VALU SQ_WAIT_INST_LDS SQ_WAIT_ANY "
+              "SQ_LDS_BANK_CONFLICT GRBM_GUI_ACTIVE --output-format csv -d $OUT/fp8_sq -o run "
+              "-- python bench.py --fp8 --steps 3 --warmup 1 --settle-ms 0",
+    "fp8_sq2": "rocprofv3 --pmc SQ_INSTS_VALU SQ_INSTS_MFMA SQ_INSTS_LDS SQ_INSTS_SALU "
+               "SQ_ACTIVE_INST_LDS SQ_INSTS_VALU_TRANS_F32 SQ_ACTIVE_INST_ANY GRBM_GUI_ACTIVE "
+               "--output-format csv -d $OUT/fp8_sq2 -o run "
+               "-- python bench.py --fp8 --steps 3 --warmup 1 --settle-ms 0",
     "decode_gqa": "rocprofv3 --kernel-trace --stats --output-format csv -d $OUT/decode_gqa -o run "
                   "-- python bench.py --decode 131072 --hkv 8",
     "decode_mha": "rocprofv3 --kernel-trace --stats --output-format csv -d $OUT/decode_mha -o run "
@@ -247,6 +263,10 @@ TRACE_ONLY = {"decode_gqa": "fa_fwd_gqa_decode_b1_h32_hkv8_nk131072_d128",
               "bwd": "fa_bwd_bf16_n16k_d128_causal_amplified",
               "fp8": "fa_fwd_fp8_bf16_n16k_d128_causal_amplified",
               "gqa": "fa_fwd_gqa_hkv8_bf16_n16k_d128_causal_amplified"}
+# counter steps of other paths, summarised kernel by kernel: summary name ->
+# (steps, kernel-name key)
+COUNTERS_ONLY = {"fa_bwd_bf16_n16k_d128_causal_amplified": (("bwd_sq", "bwd_sq2"), "fa::(anonymous namespace)::bwd_"),
+                 "fa_fwd_fp8_bf16_n16k_d128_causal_amplified": (("fp8_sq", "fp8_sq2"), "fa::(anonymous namespace)::fwd_fp8")}
 # the forward kernels of fa_fwd and fa_fwd_f32 (the summary's own kernel)
 KERNEL_KEY = "fa::(anonymous namespace)::fwd_"
 COPY_KEY = "copy"
@@ -358,6 +378,38 @@ def summarize(out_dir, workload_name, wl=4):
             f.write("# rocprofv3 counters per launch, workload %s (kernel source %s)\n" % (workload_name, src_hash))
             f.write("# commands:\n#   %s\n#   %s\n" % (profile_command("sq", wl), profile_command("sq2", wl)))
             f.write("\n".join(sq_lines) + "\n")
+    # counters of other paths, per kernel
+    for name, (steps_, key) in COUNTERS_ONLY.items():
+        per_kernel = {}
+        for part in steps_:
+            for f in glob.glob(os.path.join(out_dir, part, "**", "*counter_collection.csv"), recursive=True):
+                with open(f) as fh:
+                    for row in csv.DictReader(fh):
+                        if key not in row["Kernel_Name"]:
+                            continue
+                        kern = row["Kernel_Name"].replace("(anonymous namespace)::", "").split("(")[0]
+                        kern = kern.replace("void ", "")
+                        d = per_kernel.setdefault(kern, {}).setdefault(row["Counter_Name"], {})
+                        d[row["Dispatch_Id"]] = d.get(row["Dispatch_Id"], 0.0) + float(row["Counter_Value"])
+        if not per_kernel:
+            continue
+        out = []
+        for kern in sorted(per_kernel):
+            c = {k: float(np.mean(list(v.values()))) for k, v in per_kernel[kern].items()}
+            out.append("kernel: %s" % kern)
+            out += ["  %-28s %.4g" % (k, c[k]) for k in sorted(c)]
+            gui = c.get("GRBM_GUI_ACTIVE", 0.0) / 8.0
+            if gui and "SQ_VALU_MFMA_BUSY_CYCLES" in c:
+                out.append("  derived: MFMA busy = %.1f %%, VALU+MFMA co-issue = %.1f %%" % (
+                    100 * c["SQ_VALU_MFMA_BUSY_CYCLES"] / (gui * 1024),
+                    100 * c.get("SQ_VALU_MFMA_COEXEC_CYCLES", 0) / (gui * 1024)))
+            if c.get("SQ_INSTS_MFMA"):
+                out.append("  derived: non-MFMA VALU instructions per MFMA = %.2f" % (
+                    (c.get("SQ_INSTS_VALU", 0) - c["SQ_INSTS_MFMA"]) / c["SQ_INSTS_MFMA"]))
+        with open(os.path.join(prof, "%s_counters.txt" % name), "w") as f:
+            f.write("# rocprofv3 counters per launch, per kernel, %s (kernel source %s)\n" % (name, src_hash))
+            f.write("# commands:\n" + "".join("#   %s\n" % PROFILE_STEPS[p] for p in steps_))
+            f.write("\n".join(out) + "\n")
     # kernel-only traces of other calls (every kernel of the call)
     for step, name in TRACE_ONLY.items():
         st = _kernel_stats(os.path.join(out_dir, step), "fa::")
@@ -645,8 +697,12 @@ def main():
                      w.B, w.H, w.N, w.N, w.d, w.scale, int(w.causal), splits, ws.data_ptr(),
                      ws.numel(), stream.cuda_stream)
 
+    # the library's own ctypes entry point, without the wrapper's lookup: at
+    # C2's ~10 us per launch the Python side of a call is not negligible
+    raw = getattr(fa.load(), f.__name__)
+
     def step():
-        st = f(*call_args)
+        st = raw(*call_args)
         if st != 0:
             raise fa.FaError(st, f.__name__)
 

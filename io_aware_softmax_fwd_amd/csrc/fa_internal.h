@@ -104,14 +104,18 @@ constexpr int kTileRows = 128;
 // head, G query heads per K/V head) weigh 1..tph, so the heaviest of `splits`
 // key chunks is tph/splits of a head's G*tph^2/2; an XCD holds 64 workgroups
 // at once (32 CUs, two each).  The group is sized so the heaviest block takes
-// at most half of a group's time.
+// at most a group's time per slot (G*tph^2/2 * hg / 64): a list-scheduling
+// simulation of the dispatch and the measured times agree that the makespan
+// then stays at its ideal (C4 runs one head at a time per XCD at the same
+// speed as two, with a third of the memory traffic; C3, four heads at a
+// time, is 3 % faster than with all eight).
 inline int xcd_head_group(int64_t BH, int64_t qtiles, int G, int tph, int splits) {
   if (BH % 8 != 0 || qtiles <= 1) return 0;
   const int hx = (int)(BH / 8);   // heads per XCD
   if (tph == 0) return 1;         // equal tiles
   constexpr int64_t kXcdSlots = 64;
   const int64_t den = (int64_t)splits * G * tph;
-  const int64_t need = (4 * kXcdSlots + den - 1) / den;
+  const int64_t need = (2 * kXcdSlots + den - 1) / den;
   int g = need >= hx ? hx : (int)need;
   while (hx % g != 0) ++g;
   return g;
