@@ -286,6 +286,28 @@ int fa_fwd_fp8(const void* q8, const void* qs, const void* k8, const void* ks, c
                int causal, hipStream_t stream);
 
 /*
+ * Rotated quantization of Q or K rows (incoherent processing: the notes page
+ * "FlashAttention 原理是什么", sections 10 item ③ and 12.2, pairs block
+ * quantization with an orthogonal transform that spreads outlier channels
+ * over all head dims before rounding, since Q R (K R)^T = Q K^T for
+ * orthogonal R).  Each row x is replaced by x diag(s) H_d, with H_d the
+ * Sylvester-Hadamard matrix of order d (H_1 = [1], H_2n = [[H_n, H_n],
+ * [H_n, -H_n]]; entries +-1, H H^T = d I) and s a sign per head dim, then
+ * quantized exactly as fa_quantize_qk_fp8 does.  The transform is computed
+ * exactly in double precision (exact while the magnitudes of a row span less
+ * than 2^38) and rounded once to float before the block scales are chosen;
+ * an exact zero is +0 (code 0x00).
+ *   signs : device pointer to d bytes, entry c < 0 flips head dim c; NULL
+ *           for no flips.  Q and K must be rotated with the same signs.
+ * Since (Q R)(K R)^T = d Q K^T, attention over rotated Q and K is
+ * fa_fwd_fp8 (or fa_fwd_fp8_gqa) with scale / d (d a power of two, so the
+ * division is exact); V is not rotated.  Other arguments, layout and errors
+ * as for fa_quantize_qk_fp8 (the signs must not overlap x8 or xs).
+ */
+int fa_quantize_qk_fp8_rotated(const void* x, int64_t rows, int d, const signed char* signs,
+                               void* x8, void* xs, hipStream_t stream);
+
+/*
  * fp8 forward with grouped K/V heads (MQA/GQA, as fa_fwd_gqa with
  * Nq = Nk = N): q8, qs for the [B*H*N, d] rows of Q; k8, ks for the
  * [B*Hkv*N, d] rows of K and v8t, vs for the B*Hkv heads of V, as the

@@ -10,6 +10,7 @@ from .binding import (EXPORTED, FA_ERR_ALIAS, FA_ERR_ALIGN, FA_ERR_CAUSAL,  # no
                       bwd, bwd_gqa, fa_bwd, fa_bwd_gqa, fa_bwd_gqa_workspace_size,
                       fa_bwd_workspace_size, fa_fp8_v_bytes, fa_fp8_v_scale_bytes,
                       fa_fwd, fa_fwd_f32, fa_fwd_fp8, fa_fwd_fp8_gqa, fa_fwd_gqa, fa_quantize_qk_fp8,
+                      fa_quantize_qk_fp8_rotated,
                       fa_quantize_v_fp8, fwd_fp8, quantize_qk_fp8, quantize_v_fp8, fa_fwd_gqa_num_splits, fa_fwd_splitkv,
                       fa_fwd_splitkv_noalloc, fa_fwd_splitkv_noalloc_max_bytes,
                       fa_fwd_splitkv_num_splits, fa_fwd_splitkv_workspace_size, fa_strerror, fwd,

@@ -24,6 +24,7 @@ Low level (same names and arguments as the C functions, raw pointers):
                causal, workspace, workspace_bytes, stream)     -> status
     fa_bwd_gqa_workspace_size(B, H, Hkv, N, d)                 -> bytes
     fa_quantize_qk_fp8(x, rows, d, x8, xs, stream)             -> status
+    fa_quantize_qk_fp8_rotated(x, rows, d, signs, x8, xs, stream) -> status
     fa_quantize_v_fp8(v, BH, N, d, v8t, vs, stream)            -> status
     fa_fp8_v_bytes(BH, N, d), fa_fp8_v_scale_bytes(BH, N, d)   -> bytes
     fa_fwd_fp8(q8, qs, k8, ks, v8t, vs, o, lse, B, H, N, d, scale, causal,
@@ -41,7 +42,7 @@ High level (torch tensors on a ROCm device):
         workspace=None)                                        -> (dq, dk, dv)
     bwd_gqa(q, k, v, o, lse, dout, scale=None, causal=False,
             workspace=None)                                    -> (dq, dk, dv)
-    quantize_qk_fp8(x)                                         -> (x8, xs)
+    quantize_qk_fp8(x, signs=None, rotate=False)               -> (x8, xs)
     quantize_v_fp8(v)                                          -> (v8t, vs)
     fwd_fp8(q8, qs, k8, ks, v8t, vs, scale=None, causal=False) -> (o, lse)
 The high-level functions check every tensor they are given (type, device,
@@ -71,7 +72,7 @@ FA_ERR_SCRATCH = 12
 EXPORTED = ("fa_fwd", "fa_fwd_f32", "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_size",
             "fa_fwd_splitkv_num_splits", "fa_fwd_splitkv_noalloc", "fa_fwd_splitkv_noalloc_max_bytes",
             "fa_fwd_gqa", "fa_fwd_gqa_num_splits", "fa_bwd",
-            "fa_bwd_workspace_size", "fa_bwd_gqa", "fa_bwd_gqa_workspace_size", "fa_quantize_qk_fp8", "fa_quantize_v_fp8", "fa_fp8_v_bytes",
+            "fa_bwd_workspace_size", "fa_bwd_gqa", "fa_bwd_gqa_workspace_size", "fa_quantize_qk_fp8", "fa_quantize_qk_fp8_rotated", "fa_quantize_v_fp8", "fa_fp8_v_bytes",
             "fa_fp8_v_scale_bytes", "fa_fwd_fp8", "fa_fwd_fp8_gqa", "fa_strerror")
 
 _lib = None
@@ -159,6 +160,9 @@ def load():
     lib.fa_quantize_qk_fp8.restype = ctypes.c_int
     lib.fa_quantize_qk_fp8.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p,
                                        ctypes.c_void_p, ctypes.c_void_p]
+    lib.fa_quantize_qk_fp8_rotated.restype = ctypes.c_int
+    lib.fa_quantize_qk_fp8_rotated.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p,
+                                               ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
     lib.fa_quantize_v_fp8.restype = ctypes.c_int
     lib.fa_quantize_v_fp8.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                       ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
@@ -241,6 +245,10 @@ def fa_bwd_gqa_workspace_size(B, H, Hkv, N, d):
 
 def fa_quantize_qk_fp8(x, rows, d, x8, xs, stream):
     return load().fa_quantize_qk_fp8(x, rows, d, x8, xs, stream)
+
+
+def fa_quantize_qk_fp8_rotated(x, rows, d, signs, x8, xs, stream):
+    return load().fa_quantize_qk_fp8_rotated(x, rows, d, signs, x8, xs, stream)
 
 
 def fa_quantize_v_fp8(v, BH, N, d, v8t, vs, stream):
@@ -468,9 +476,11 @@ def _bf16_4d(name, t):
         raise ValueError("%s must be [B, H, N, d]" % name)
 
 
-def quantize_qk_fp8(x, stream=None):
+def quantize_qk_fp8(x, stream=None, rotate=False, signs=None):
     """MX fp8 quantization of a bf16 [B,H,N,d] Q or K: returns (codes uint8
-    [B,H,N,d], E8M0 scales uint8 [B,H,N,d/32])."""
+    [B,H,N,d], E8M0 scales uint8 [B,H,N,d/32]).  rotate=True quantizes the
+    rows rotated by diag(signs) H_d (fa_quantize_qk_fp8_rotated); signs is
+    then None or an int8 tensor of d entries on the same device."""
     import torch
     _bf16_4d("x", x)
     B, H, N, d = x.shape
@@ -478,9 +488,20 @@ def quantize_qk_fp8(x, stream=None):
     xs = torch.empty((B, H, N, d // 32), dtype=torch.uint8, device=x.device)
     if stream is None:
         stream = torch.cuda.current_stream(x.device).cuda_stream
-    st = fa_quantize_qk_fp8(x.data_ptr(), B * H * N, d, x8.data_ptr(), xs.data_ptr(), stream)
+    if rotate:
+        sp = None
+        if signs is not None:
+            _check("signs", signs, x.device, torch.int8, (d,))
+            sp = signs.data_ptr()
+        st = fa_quantize_qk_fp8_rotated(x.data_ptr(), B * H * N, d, sp, x8.data_ptr(), xs.data_ptr(), stream)
+        name = "fa_quantize_qk_fp8_rotated"
+    else:
+        if signs is not None:
+            raise ValueError("signs are only used with rotate=True")
+        st = fa_quantize_qk_fp8(x.data_ptr(), B * H * N, d, x8.data_ptr(), xs.data_ptr(), stream)
+        name = "fa_quantize_qk_fp8"
     if st != FA_OK:
-        raise FaError(st, "fa_quantize_qk_fp8")
+        raise FaError(st, name)
     return x8, xs
 
 

@@ -283,6 +283,19 @@ int fa_quantize_qk_fp8(const void* x, int64_t rows, int d, void* x8, void* xs, h
   return fa::launch_quantize_qk_fp8(x, rows, d, x8, xs, stream) == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
+int fa_quantize_qk_fp8_rotated(const void* x, int64_t rows, int d, const signed char* signs, void* x8,
+                               void* xs, hipStream_t stream) {
+  if (!x || !x8 || !xs) return FA_ERR_NULL;
+  if (rows < 1) return FA_ERR_SHAPE;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED_D;
+  if (rows * d >= kMaxElems) return FA_ERR_SHAPE;
+  if (any_misaligned({x, x8, xs})) return FA_ERR_ALIGN;
+  const int64_t xb = rows * d * 2, cb = rows * d, sb = rows * (d / 32);
+  if (any_overlap(x8, cb, {{x, xb}, {xs, sb}}) || any_overlap(xs, sb, {{x, xb}})) return FA_ERR_ALIAS;
+  if (signs && (any_overlap(x8, cb, {{signs, d}}) || any_overlap(xs, sb, {{signs, d}}))) return FA_ERR_ALIAS;
+  return fa::launch_quantize_qk_fp8_rotated(x, rows, d, signs, x8, xs, stream) == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 size_t fa_fp8_v_bytes(int BH, int N, int d) {
   if (BH < 1 || N < 1 || (d != 64 && d != 128)) return 0;
   return (size_t)fa::fp8_v_code_bytes(BH, N, d);

@@ -100,6 +100,89 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const unsigned short* _
   xs[t] = (unsigned char)E;
 }
 
+// MX quantization of 32 fp32 values (one block) into 32 E4M3 codes, stored
+// as two 16-byte words in element order, and the block's E8M0 scale.
+__device__ __forceinline__ unsigned char mx_block32(const float (&val)[32], u32x4 (&out)[2]) {
+  unsigned amax = 0;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) amax = max(amax, __float_as_uint(val[i]) & 0x7FFFFFFFu);
+  const int E = mx_scale_exponent(amax);
+#pragma unroll
+  for (int w = 0; w < 8; ++w) {
+    int word = 0;
+    word = __builtin_amdgcn_cvt_pk_fp8_f32(mx_scaled(val[4 * w], E), mx_scaled(val[4 * w + 1], E), word, false);
+    word = __builtin_amdgcn_cvt_pk_fp8_f32(mx_scaled(val[4 * w + 2], E), mx_scaled(val[4 * w + 3], E), word, true);
+    out[w / 4][w % 4] = (unsigned)word;
+  }
+  return (unsigned char)E;
+}
+
+// Rows of Q or K rotated before quantization (incoherent processing: the
+// notes page, section 10 item ③, spreads outlier channels over all head
+// dims by an orthogonal transform; QR (KR)^T = Q K^T for orthogonal R).
+// Here R = diag(s) H_D with H_D the Sylvester-Hadamard matrix (entries
+// +-1, H H^T = D I) and s a sign per head dim, so that
+// (Q R)(K R)^T = D Q K^T: the attention on rotated inputs takes scale / D.
+// The transform is computed exactly (fp64 butterflies over bf16 inputs; the
+// sums stay exact while a row's magnitudes span fewer than 2^38) and rounded
+// once to fp32 before the block scales are chosen; an exact zero is taken as
+// +0 whatever the signs of the terms that cancelled.  D/64 threads per row
+// (adjacent lanes), each holding 64 head dims: at D = 128 the stride-64
+// butterfly pairs the two lanes through a shuffle, the rest is in-lane.
+template <int D>
+__global__ __launch_bounds__(256) void quant_rows_rot_kernel(const unsigned short* __restrict__ x, int64_t rows,
+                                                            const signed char* __restrict__ signs,
+                                                            unsigned char* __restrict__ x8,
+                                                            unsigned char* __restrict__ xs) {
+  constexpr int TPR = D / 64;
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t row = t / TPR;
+  const int part = (int)(t % TPR);
+  if (row >= rows) return;   // both lanes of a row leave together
+  const unsigned short* src = x + row * D + 64 * part;
+  double v[64];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const u32x4 raw = reinterpret_cast<const u32x4*>(src)[i];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const unsigned bits = (raw[e / 2] >> (16 * (e % 2))) & 0xFFFFu;
+      const int dim = 64 * part + 8 * i + e;
+      const double f = (double)__uint_as_float(bits << 16);
+      v[8 * i + e] = (signs != nullptr && signs[dim] < 0) ? -f : f;
+    }
+  }
+  if constexpr (TPR == 2) {
+    // H_128 = [[H_64, H_64], [H_64, -H_64]]: first (x_lo + x_hi, x_lo - x_hi)
+#pragma unroll
+    for (int i = 0; i < 64; ++i) {
+      const double o = __shfl_xor(v[i], 1, 64);
+      v[i] = part == 0 ? v[i] + o : o - v[i];
+    }
+  }
+#pragma unroll
+  for (int h = 1; h < 64; h *= 2)
+#pragma unroll
+    for (int i = 0; i < 64; ++i)
+      if ((i & h) == 0) {
+        const double a = v[i], b = v[i + h];
+        v[i] = a + b;
+        v[i + h] = a - b;
+      }
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    float val[32];
+#pragma unroll
+    for (int i = 0; i < 32; ++i) val[i] = (float)(v[32 * b + i] + 0.0);   // an exact zero is +0
+    u32x4 out[2];
+    const unsigned char E = mx_block32(val, out);
+    u32x4* dst = reinterpret_cast<u32x4*>(x8 + row * D + 64 * part + 32 * b);
+    dst[0] = out[0];
+    dst[1] = out[1];
+    xs[row * (D / 32) + 2 * part + b] = E;
+  }
+}
+
 // One thread per (head, tile, key block b, head dim c): the 32 keys
 // 64t + 32b .. +31 of dim c.  Their codes go to two 16-byte runs of tile row
 // c: positions 16b .. 16b+15 (keys with bit 2 of the key index clear) and
@@ -473,6 +556,16 @@ hipError_t launch_quant_rows(const void* x, int64_t rows, void* x8, void* xs, hi
 }
 
 template <int D>
+hipError_t launch_quant_rows_rot(const void* x, int64_t rows, const void* signs, void* x8, void* xs,
+                                 hipStream_t stream) {
+  const int64_t threads = rows * (D / 64);
+  hipLaunchKernelGGL((quant_rows_rot_kernel<D>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream,
+                     static_cast<const unsigned short*>(x), rows, static_cast<const signed char*>(signs),
+                     static_cast<unsigned char*>(x8), static_cast<unsigned char*>(xs));
+  return hipGetLastError();
+}
+
+template <int D>
 hipError_t launch_quant_v(const void* v, int BH, int N, void* v8t, void* vs, hipStream_t stream) {
   const int T = (N + kF8Keys - 1) / kF8Keys;
   const int64_t threads = (int64_t)BH * T * 2 * D;
@@ -500,6 +593,12 @@ hipError_t launch_fp8(const Fp8Problem& p, hipStream_t stream) {
 
 hipError_t launch_quantize_qk_fp8(const void* x, int64_t rows, int d, void* x8, void* xs, hipStream_t stream) {
   return d == 64 ? launch_quant_rows<64>(x, rows, x8, xs, stream) : launch_quant_rows<128>(x, rows, x8, xs, stream);
+}
+
+hipError_t launch_quantize_qk_fp8_rotated(const void* x, int64_t rows, int d, const void* signs, void* x8,
+                                          void* xs, hipStream_t stream) {
+  return d == 64 ? launch_quant_rows_rot<64>(x, rows, signs, x8, xs, stream)
+                 : launch_quant_rows_rot<128>(x, rows, signs, x8, xs, stream);
 }
 
 hipError_t launch_quantize_v_fp8(const void* v, int BH, int N, int d, void* v8t, void* vs, hipStream_t stream) {

@@ -170,6 +170,8 @@ hipError_t launch_fwd_f32(const Problem& p, hipStream_t stream);
 hipError_t launch_fwd_bf16(const GqaProblem& p, hipStream_t stream);
 hipError_t launch_bwd_bf16(const BwdProblem& p, hipStream_t stream);
 hipError_t launch_quantize_qk_fp8(const void* x, int64_t rows, int d, void* x8, void* xs, hipStream_t stream);
+hipError_t launch_quantize_qk_fp8_rotated(const void* x, int64_t rows, int d, const void* signs, void* x8,
+                                          void* xs, hipStream_t stream);
 hipError_t launch_quantize_v_fp8(const void* v, int BH, int N, int d, void* v8t, void* vs, hipStream_t stream);
 hipError_t launch_fwd_fp8(const Fp8Problem& p, hipStream_t stream);
 

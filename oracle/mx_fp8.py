@@ -27,12 +27,28 @@ with bias 7, 3 mantissa bits; exponent field 0 holds the subnormals
 m * 2^-9; the all-ones code S.1111.111 is NaN and there is no infinity, so
 the largest finite value is 1.75 * 2^8 = 448.
 
+Incoherent processing (notes page, section 10 item ③ and section 12.2):
+before block quantization, Q and K rows can be rotated by an orthogonal
+transform that spreads outlier channels over all head dims; since
+(Q R)(K R)^T = Q R R^T K^T, an orthogonal R leaves the scores unchanged.  The
+reading taken here: R = diag(s) H_d with H_d the Sylvester-Hadamard matrix of
+order d (H_1 = [1], H_2n = [[H_n, H_n], [H_n, -H_n]]), entries +-1 and
+H H^T = d I, and s a sign per head dim (an input, drawn by the caller).  It
+is not normalised, so (Q R)(K R)^T = d Q K^T and the attention over rotated
+inputs takes scale / d, an exact power-of-two change.  The rotated row is
+computed in float64 (the products by +-1 and the sums are exact for
+bf16-valued rows whose magnitudes span fewer than 2^38) and rounded once to
+float32, an exact zero taken as +0 (its sign would otherwise depend on the
+order of the sums); the MX quantization above then applies unchanged.
+
 Functions
   e4m3_decode(codes)              -> float32 values
   e4m3_encode(x)                  -> uint8 codes, x already within [-448, 448]
   mx_quantize(x, axis=-1)         -> (codes uint8, scales uint8), blocks of 32
                                      consecutive elements along `axis`
   mx_dequantize(codes, scales, axis=-1) -> float32
+  hadamard(d)                     -> float64 [d, d] Sylvester-Hadamard matrix
+  rotate_rows(x, signs=None)      -> float32 rows of x diag(signs) H_d
 """
 import numpy as np
 
@@ -109,3 +125,25 @@ def mx_dequantize(codes, scales, axis=-1):
     out = np.ldexp(cb, (E - 127)[..., None].astype(np.int32)).astype(np.float32)
     out = out.reshape(out.shape[:-2] + (-1,))
     return np.moveaxis(out, -1, axis)
+
+
+def hadamard(d):
+    """The Sylvester-Hadamard matrix of order d (a power of two), float64."""
+    if d < 1 or d & (d - 1):
+        raise ValueError("d must be a power of two")
+    h = np.ones((1, 1))
+    while h.shape[0] < d:
+        h = np.block([[h, h], [h, -h]])
+    return h
+
+
+def rotate_rows(x, signs=None):
+    """x diag(signs) H_d along the last axis (d = x.shape[-1]), in float64,
+    rounded once to float32.  signs: d values, an entry < 0 flips that head
+    dim; None flips none."""
+    x = np.asarray(x, dtype=np.float32).astype(np.float64)
+    d = x.shape[-1]
+    if signs is not None:
+        x = x * np.where(np.asarray(signs) < 0, -1.0, 1.0)
+    # an exact zero is +0, whichever signed zeros or terms produced it
+    return (x @ hadamard(d) + 0.0).astype(np.float32)

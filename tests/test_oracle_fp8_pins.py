@@ -4,6 +4,7 @@ an exhaustive nearest-value search, and the scaling identities."""
 import numpy as np
 import pytest
 
+from io_aware_softmax_fwd_amd import workloads as W
 from oracle import mx_fp8 as mx
 
 
@@ -120,3 +121,66 @@ def test_planted_encoder_mistake_is_caught():
     mids = ((pos[:-1] + pos[1:]) / 2).astype(np.float32)
     away = np.searchsorted(pos, mids.astype(np.float64), side="left").astype(np.uint8)
     assert not np.array_equal(away, _nearest_brute(mids))
+
+
+# ------------------------------------------------- incoherent processing
+def test_hadamard_small_orders_written_out():
+    assert np.array_equal(mx.hadamard(1), [[1.0]])
+    assert np.array_equal(mx.hadamard(2), [[1, 1], [1, -1]])
+    assert np.array_equal(mx.hadamard(4), [[1, 1, 1, 1], [1, -1, 1, -1], [1, 1, -1, -1], [1, -1, -1, 1]])
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_hadamard_closed_form_and_orthogonality(d):
+    """Entry (i, j) of the Sylvester construction is (-1)^popcount(i & j),
+    and H H^T = d I."""
+    h = mx.hadamard(d)
+    i, j = np.meshgrid(np.arange(d), np.arange(d), indexing="ij")
+    parity = np.vectorize(lambda a: bin(a).count("1") & 1)(i & j)
+    assert np.array_equal(h, np.where(parity == 1, -1.0, 1.0))
+    assert np.array_equal(h @ h.T, d * np.eye(d))
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_rotation_preserves_scores_up_to_d(d):
+    """(q R)(k R)^T = d q k^T with R = diag(s) H: exact in float64 for
+    bf16-valued rows, so the float32 rounding of the rotated rows is the
+    only difference; rotating back (R^T / d) recovers the row."""
+    rng = np.random.default_rng(d)
+    bf = lambda a: W.bf16_bits_to_f32(W.bf16_bits_rne(a.astype(np.float32)))
+    q = bf(rng.standard_normal((20, d)))
+    k = bf(rng.standard_normal((30, d)))
+    s = np.where(rng.random(d) < 0.5, -1, 1).astype(np.int8)
+    qr, kr = mx.rotate_rows(q, s), mx.rotate_rows(k, s)
+    exact = d * (q.astype(np.float64) @ k.astype(np.float64).T)
+    got = qr.astype(np.float64) @ kr.astype(np.float64).T
+    # each rotated entry carries at most half an fp32 ulp of relative error
+    bound = 2.0 ** -23 * (np.abs(qr).astype(np.float64) @ np.abs(kr).astype(np.float64).T)
+    assert np.all(np.abs(got - exact) <= bound)
+    back = (qr.astype(np.float64) @ mx.hadamard(d).T / d) * np.where(s < 0, -1.0, 1.0)
+    assert np.allclose(back, q, rtol=0, atol=2.0 ** -20 * np.abs(q).max())
+    # without signs the first column of H is all ones: entry 0 is the row sum
+    r0 = mx.rotate_rows(q)
+    assert np.array_equal(r0[:, 0], q.astype(np.float64).sum(axis=1).astype(np.float32))
+
+
+def test_rotation_spreads_an_outlier_channel():
+    """A row that is zero except one head dim becomes a row of equal
+    magnitudes: the outlier is spread over all d dims (so one E4M3 block
+    scale no longer has to cover it alone)."""
+    d = 128
+    x = np.zeros((1, d), dtype=np.float32)
+    x[0, 37] = 50.0
+    r = mx.rotate_rows(x)
+    assert np.array_equal(np.abs(r), np.full((1, d), 50.0, dtype=np.float32))
+
+
+def test_rotation_of_signed_zeros_is_plus_zero():
+    """A zero row, with any signs, rotates to +0 in every dim (code 0x00)."""
+    x = np.zeros((2, 64), dtype=np.float32)
+    x[1] = -0.0
+    s = np.where(np.arange(64) % 3 == 0, -1, 1).astype(np.int8)
+    r = mx.rotate_rows(x, s)
+    assert np.all(r == 0) and not np.any(np.signbit(r))
+    c, e = mx.mx_quantize(r)
+    assert np.all(c == 0) and np.all(e == 0)
