@@ -73,6 +73,13 @@ enum fa_status {
  *   stream  : HIP stream the kernel is queued on.
  * Products are taken on bf16 matrix cores with fp32 accumulation; the
  * softmax statistics, the rescaling and the final division are fp32.
+ * Range of V: the exponent offset may lag the running row max, so a tile's
+ * unnormalised probabilities can reach 2^48 before the offset moves, and
+ * the fp32 output accumulators can reach about 2^79 * max|v| (fewer than
+ * 2^31 keys).  O is finite and within the stated accuracy for
+ * max|v| < 2^48 (about 2.8e14); beyond that the accumulators may overflow
+ * to inf or NaN where the exact result is finite.  Q and K have no such
+ * limit (the scores themselves are exact fp32 products of bf16 values).
  * Returns an fa_status.
  */
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
