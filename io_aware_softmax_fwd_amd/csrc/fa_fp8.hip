@@ -584,7 +584,7 @@ hipError_t launch_fp8(const Fp8Problem& p, hipStream_t stream) {
                      static_cast<const unsigned char*>(p.qs), static_cast<const unsigned char*>(p.k8),
                      static_cast<const unsigned char*>(p.ks), static_cast<const unsigned char*>(p.v8t),
                      static_cast<const unsigned char*>(p.vs), static_cast<unsigned short*>(p.o), p.lse, p.N,
-                     BH, n_qtiles, p.scale, xcd_head_group(BH, n_qtiles, 1, CAUSAL ? n_qtiles : 0, 1),
+                     BH, n_qtiles, p.scale, xcd_head_group(BH, n_qtiles, 1, CAUSAL ? n_qtiles : 0, 1, 4),
                      p.H, p.H / p.Hkv);
   return hipGetLastError();
 }

@@ -109,13 +109,17 @@ constexpr int kTileRows = 128;
 // then stays at its ideal (C4 runs one head at a time per XCD at the same
 // speed as two, with a third of the memory traffic; C3, four heads at a
 // time, is 3 % faster than with all eight).
-inline int xcd_head_group(int64_t BH, int64_t qtiles, int G, int tph, int splits) {
+// `spread` scales that bound: the fp8 kernel, which is not held by the power
+// limit and so is bound by cycles rather than by data movement, keeps the
+// heaviest block to half a group's time (spread 4; C4 fp8 3 % faster than at
+// spread 2).
+inline int xcd_head_group(int64_t BH, int64_t qtiles, int G, int tph, int splits, int spread = 2) {
   if (BH % 8 != 0 || qtiles <= 1) return 0;
   const int hx = (int)(BH / 8);   // heads per XCD
   if (tph == 0) return 1;         // equal tiles
   constexpr int64_t kXcdSlots = 64;
   const int64_t den = (int64_t)splits * G * tph;
-  const int64_t need = (2 * kXcdSlots + den - 1) / den;
+  const int64_t need = (spread * kXcdSlots + den - 1) / den;
   int g = need >= hx ? hx : (int)need;
   while (hx % g != 0) ++g;
   return g;
