@@ -57,7 +57,7 @@ class Workload:
         return ("B=%d H=%d N=%d d=%d %s %s%s" % (
             self.B, self.H, self.N, self.d, self.dtype,
             "causal" if self.causal else "non-causal",
-            ", 1%% rows x8" if self.amplify else ""))
+            ", 1% rows x8" if self.amplify else ""))
 
 
 WORKLOADS = {
