@@ -294,8 +294,9 @@ struct Fwd {
 
   // One pipeline step: queue tile j+1 into the other buffers (it gets the
   // whole step to land), consume tile j, wait and synchronise.
-  // PAR = j & 1 selects the buffers at compile time.
-  template <bool MASK, int PAR>
+  // PAR = j & 1 selects the buffers at compile time; FIRST marks the
+  // workgroup's first tile.
+  template <bool MASK, int PAR, bool FIRST = false>
   __device__ void step(int j, int t_end) {
     const int k0 = j * kKeys;
     if (j + 1 < t_end) {
@@ -305,7 +306,7 @@ struct Fwd {
     // Causal: a wave whose last query precedes the tile's first key has
     // nothing to do here or later; key chunks of a decoding step leave whole
     // waves without a query row.  The barrier below stays unconditional.
-    if ((!SPLIT || rows) && (!MASK || !CAUSAL || k0 <= wlast)) consume<MASK, PAR>(k0);
+    if ((!SPLIT || rows) && (!MASK || !CAUSAL || k0 <= wlast)) consume<MASK, PAR, FIRST>(k0);
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
     __builtin_amdgcn_s_barrier();
   }
@@ -427,15 +428,20 @@ __global__ __launch_bounds__(kThreads, (QB == 1 || D == 64) ? 2 : 1) void fwd_bf
     f.template issue<true, 0>(t0 * kKeys);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    // buffer parity counts from t0
+    // buffer parity counts from t0.  The first tile goes straight to the
+    // row max (the offset is still -inf), skipping the probability pass that
+    // would be discarded.
     int j = t0;
     const int full_end = max(t0, min(t1, n_full));
+    if (j < full_end) f.template step<false, 0, true>(j, t1);
+    else              f.template step<true, 0, true>(j, t1);
+    ++j;
     for (; j + 1 < full_end; j += 2) {
-      f.template step<false, 0>(j, t1);
-      f.template step<false, 1>(j + 1, t1);
+      f.template step<false, 1>(j, t1);
+      f.template step<false, 0>(j + 1, t1);
     }
     if (j < full_end) {
-      f.template step<false, 0>(j, t1);
+      f.template step<false, 1>(j, t1);
       ++j;
     }
     for (; j < t1; ++j) {
@@ -730,13 +736,16 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void fwd_bf16_ws_kernel(
 // Merge of the key chunks of every row: LSE = log sum_s exp(LSE_s) and
 // O = sum_s exp(LSE_s - LSE) O_s, the online-softmax merge applied to whole
 // chunks (zzszmyf.github.io notes, sections 5 and 12.1).  One workgroup per
-// row, sized so that each lane reads about kMergeBatch chunks: a lane reads
-// four head dims of a chunk with one 16-byte load (one wave-wide load covers
-// 256/D chunks) and issues kMergeBatch such loads before it waits, so a row's
-// chunks arrive in one or two memory latencies rather than one after another.
-// Each lane keeps its own running max (the same online rescaling), and the
-// lanes meet at the row max: lane groups through shuffles, waves in LDS.
-// Chunk 0 always holds key 0, so the row max is finite.
+// (row, slice of D/DS head dims), sized so that each lane reads about
+// kMergeBatch chunks: a lane reads four head dims of a chunk with one 16-byte
+// load (one wave-wide load covers 256 DS/D chunks) and issues kMergeBatch
+// such loads before it waits, so a row's chunks arrive in one or two memory
+// latencies rather than one after another.  Each lane keeps its own running
+// max (the same online rescaling), and the lanes meet at the row max: lane
+// groups through shuffles, waves in LDS.  Every slice of a row reads all of
+// the row's chunk LSEs, so it has the row max and the denominator itself;
+// DS > 1 spreads the few rows of a decoding step over more CUs.  Chunk 0
+// always holds key 0, so the row max is finite.
 constexpr int kMergeMaxWaves = 16;
 constexpr int kMergeBatch = 8;
 
@@ -746,24 +755,27 @@ __device__ __forceinline__ float wave_max(float x) {
   return x;
 }
 
-// Waves per merge workgroup for `splits` chunks of D dims.
-template <int D>
+// Waves per merge workgroup for `splits` chunks of D/DS dims.
+template <int D, int DS>
 int merge_waves(int splits) {
-  const int64_t lanes = (int64_t)splits * (D / 4);
+  const int64_t lanes = (int64_t)splits * (D / DS / 4);
   return (int)std::max<int64_t>(1, std::min<int64_t>(kMergeMaxWaves, (lanes + 64 * kMergeBatch - 1) / (64 * kMergeBatch)));
 }
 
-template <int D>
+template <int D, int DS>
 __global__ __launch_bounds__(64 * kMergeMaxWaves) void merge_kernel(const float* __restrict__ opart,
                                                                    const float* __restrict__ lpart,
                                                                    unsigned short* __restrict__ o,
                                                                    float* __restrict__ lse,
                                                                    int64_t rows, int splits) {
-  constexpr int LPS = D / 4;          // lanes per chunk row, four dims each
+  constexpr int DW = D / DS;          // head dims of this workgroup
+  constexpr int LPS = DW / 4;         // lanes per chunk row, four dims each
   constexpr int SPI = 64 / LPS;       // chunks per wave-wide load
+  static_assert(LPS >= 1 && LPS <= 64 && DW % 4 == 0, "merge slice width");
   __shared__ float red[kMergeMaxWaves];
   __shared__ float4 part[kMergeMaxWaves][LPS];
-  const int64_t row = blockIdx.x;
+  const int64_t row = blockIdx.x / DS;
+  const int dim0 = DW * (int)(blockIdx.x % DS);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int nw = blockDim.x >> 6;
   const int step = nw * SPI;          // chunks per pass of the workgroup
@@ -779,7 +791,7 @@ __global__ __launch_bounds__(64 * kMergeMaxWaves) void merge_kernel(const float*
     for (int u = 0; u < kMergeBatch; ++u) {
       const int64_t sp = min(base + u * step, splits - 1);
       ls[u] = lpart[sp * rows + row];
-      a[u] = *reinterpret_cast<const float4*>(opart + (sp * rows + row) * D + 4 * c4);
+      a[u] = *reinterpret_cast<const float4*>(opart + (sp * rows + row) * D + dim0 + 4 * c4);
     }
     float mb = m;
 #pragma unroll
@@ -842,8 +854,8 @@ __global__ __launch_bounds__(64 * kMergeMaxWaves) void merge_kernel(const float*
   }
   const float inv = 1.f / tot;
   const u32x2 out = {pack_bf16x2(t.x * inv, t.y * inv), pack_bf16x2(t.z * inv, t.w * inv)};
-  *reinterpret_cast<u32x2*>(o + row * D + 4 * lane) = out;
-  if (lane == 0) lse[row] = M + logf(tot);
+  *reinterpret_cast<u32x2*>(o + row * D + dim0 + 4 * lane) = out;
+  if (lane == 0 && dim0 == 0) lse[row] = M + logf(tot);
 }
 
 // The same merge for many rows: one thread per (row, 8 head dims), each
@@ -881,6 +893,16 @@ __global__ __launch_bounds__(256) void merge_rows_kernel(const float* __restrict
 
 // Rows above which the merge runs one thread per (row, 8 dims).
 constexpr int64_t kMergeRowsMin = 4096;
+// Below it, a row's head dims are split over up to D/16 workgroups until the
+// merge has at least this many.
+constexpr int64_t kMergeMinGrid = 256;
+
+template <int D, int DS>
+void launch_merge(const float* opart, const float* lpart, unsigned short* o, float* lse, int64_t rows,
+                  int splits, hipStream_t stream) {
+  hipLaunchKernelGGL((merge_kernel<D, DS>), dim3((unsigned)(rows * DS)), dim3(64 * merge_waves<D, DS>(splits)), 0,
+                     stream, opart, lpart, o, lse, rows, splits);
+}
 // Up to this many 128-row workgroups (three quarters of the 256 CUs) a call
 // with at least kWsMinTiles key tiles runs fwd_bf16_ws_kernel instead:
 // 32-row workgroups whose four waves split the keys.  Measured against the
@@ -951,8 +973,11 @@ hipError_t launch(const GqaProblem& p, hipStream_t stream) {
     hipLaunchKernelGGL((merge_rows_kernel<D>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
                        stream, opart, lpart, static_cast<unsigned short*>(p.o), p.lse, rows, p.splits);
   } else {
-    hipLaunchKernelGGL((merge_kernel<D>), dim3((unsigned)rows), dim3(64 * merge_waves<D>(p.splits)), 0, stream, opart,
-                       lpart, static_cast<unsigned short*>(p.o), p.lse, rows, p.splits);
+    unsigned short* o = static_cast<unsigned short*>(p.o);
+    if (rows * 4 < kMergeMinGrid && D >= 128) launch_merge<D, D / 16>(opart, lpart, o, p.lse, rows, p.splits, stream);
+    else if (rows * 2 < kMergeMinGrid) launch_merge<D, 4>(opart, lpart, o, p.lse, rows, p.splits, stream);
+    else if (rows < kMergeMinGrid) launch_merge<D, 2>(opart, lpart, o, p.lse, rows, p.splits, stream);
+    else launch_merge<D, 1>(opart, lpart, o, p.lse, rows, p.splits, stream);
   }
   return hipGetLastError();
 }

@@ -47,6 +47,11 @@ CASES = [
     (1, 3, 130, 100, 128, False, 5),     # more chunks than key tiles
     (1, 1, 1, 1, 64, True, 2),
     (1, 2, 256, 300, 128, True, 6),
+    # few rows: the merge splits a row's head dims over 8, 4 or 2 workgroups
+    (1, 8, 1, 17000, 128, True, 256),
+    (1, 8, 12, 3000, 128, True, 9),
+    (1, 3, 50, 2000, 128, False, 11),
+    (1, 16, 2, 2500, 64, True, 17),
 ]
 
 
