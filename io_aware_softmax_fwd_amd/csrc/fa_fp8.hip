@@ -276,10 +276,19 @@ struct FwdF8 {
   int koff[C::kDmaPerWave], voff[C::vDmaPerWave];
   int k_rd[2 * KS];             // K read offset of chunk 4 ks + 2 h + hl, index 2 ks + h
   int v_rd[2];                 // V^T read offset of chunk 2 hl + h, index h
-  unsigned ksw[2][2];          // K scale words of the key rows 32kb + l32, per buffer
-  unsigned vsw[2];             // V scale word (byte db) per buffer
+  unsigned ksw[2][2];          // d = 64: K scale words of the key rows 32kb + l32, per buffer
+  unsigned ksel;               // v_perm selector: the scale bytes of blocks hl (and 2 + hl)
+  int vs_bytes;                // bytes of the head's V scales (whole tiles)
   unsigned char* kbuf[2];
   unsigned char* vbuf[2];
+  // Scale words of the tile per buffer (in the K buffer, after the codes),
+  // queued by LDS-DMA with the codes: V (entry l for lane l) and, at
+  // d = 128, K (key rows r and 32 + r side by side).
+  // Held in registers instead, the words of the next tile were copied
+  // between registers across the unrolled loop, and the compiler then
+  // waited for every load in flight, the next tile's codes included.
+  unsigned char* vsbuf[2];
+  unsigned char* ksbuf[2];
 
   // Queue tile k0 into buffer B: K and V^T codes by LDS-DMA, scale words
   // into registers.
@@ -303,19 +312,31 @@ struct FwdF8 {
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(vbuf[B] + blk * 1024), 16, voff[i], 0, 0, 0);
     }
 #endif
+#if defined(__HIP_DEVICE_COMPILE__)
+    // K scales of keys k0.. (range-checked: keys past N read 0)
+    const __amdgpu_buffer_rsrc_t rks = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(ksh + (int64_t)k0 * (D / 32)), (short)0, (N - k0) * (D / 32), 0x00020000);
+    if constexpr (D == 128) {
+      // LDS word i holds key row 32 (i % 2) + i / 2, so the two rows a lane
+      // reads (l32 and 32 + l32) are one 8-byte read
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rks, (lds_void*)ksbuf[B], 4, 4 * (32 * (l32 & 1) + 16 * hl + (l32 >> 1)), 0, 0, 0);
+    } else {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const int key = k0 + 32 * kb + l32;
-      unsigned w = 0;
-      if (key < N) {
-        if constexpr (D == 128) w = *reinterpret_cast<const unsigned*>(ksh + (int64_t)key * 4);
-        else w = *reinterpret_cast<const unsigned short*>(ksh + (int64_t)key * 2);
-      }
-      ksw[B][kb] = w;
+      for (int kb = 0; kb < 2; ++kb)
+        ksw[B][kb] = __builtin_amdgcn_raw_buffer_load_b16(rks, 2 * (32 * kb + l32), 0, 0);
     }
-    const int64_t vsrow = ((int64_t)(k0 / kF8Keys) * 2 + hl) * 32 + l32;
-    if constexpr (D == 128) vsw[B] = *reinterpret_cast<const unsigned*>(vsh + vsrow * 4);
-    else vsw[B] = *reinterpret_cast<const unsigned short*>(vsh + vsrow * 2);
+    // the tile's 64 V scale entries of D/32 bytes, one dword per lane (the
+    // range ends with the head's last tile).  Every wave queues the same
+    // scale words to the same place: the copies are identical, and a load
+    // that depends on the wave would make the compiler wait for every load
+    // in flight before each read of LDS.
+    {
+      const int off = (k0 / kF8Keys) * 64 * (D / 32);
+      const __amdgpu_buffer_rsrc_t rs =
+          __builtin_amdgcn_make_buffer_rsrc((void*)(vsh + off), (short)0, vs_bytes - off, 0x00020000);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)vsbuf[B], 4, 4 * (32 * hl + l32), 0, 0, 0);
+    }
+#endif
   }
 
   template <bool MASK, int PAR>
@@ -323,14 +344,16 @@ struct FwdF8 {
     const unsigned char* kt = kbuf[PAR];
     const unsigned char* vt = vbuf[PAR];
     f32x16 s[2];
+    // d = 128: the scale words of key rows l32 and 32 + l32, adjacent in LDS
+    u32x2 kw = {0u, 0u};
+    if constexpr (D == 128) kw = reinterpret_cast<const u32x2*>(ksbuf[PAR])[l32];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
       // scale word of this lane's key row: byte ks = block 2*ks + hl
-      const unsigned w = ksw[PAR][kb];
-      const unsigned ksc = D == 128 ? (((w >> (8 * hl)) & 0xFF) | (((w >> (16 + 8 * hl)) & 0xFF) << 8))
-                                    : ((w >> (8 * hl)) & 0xFF);
+      const unsigned w = D == 128 ? kw[kb] : ksw[PAR][kb];
+      const unsigned ksc = __builtin_amdgcn_perm(w, w, ksel);
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         const unsigned char* src = kt + 32 * kb * C::kStride;
@@ -392,7 +415,9 @@ struct FwdF8 {
     const i32x8 ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838,
                         0x38383838, 0x38383838, 0x38383838, 0x38383838};
     lacc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones, pf, lacc, 0, 0, 0, kUnitScale, 0, kUnitScale);
-    const unsigned vsc = vsw[PAR];
+    const int ln = 32 * hl + l32;
+    const unsigned vsc = D == 128 ? reinterpret_cast<const unsigned*>(vsbuf[PAR])[ln]
+                                  : reinterpret_cast<const unsigned short*>(vsbuf[PAR])[ln];
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
       const unsigned char* src = vt + 32 * db * C::vStride;
@@ -417,6 +442,14 @@ struct FwdF8 {
     if (!MASK || !CAUSAL || k0 <= qw + 31) consume<MASK, PAR>(k0);
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
     __builtin_amdgcn_s_barrier();
+    // A VALU read of a v_mfma_scale_f32_32x32x64_f8f6f4 result needs 20 wait
+    // states on the MI355X (measured: at 19 the last result registers still
+    // hold their old values), one more than the compiler counts.  The
+    // register copies it places where the tile loops exit read the last
+    // tile's accumulators; these four wait states, which no product of the
+    // step may be moved past, keep such copies far enough behind.
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_nop 3" ::: "memory");
   }
 };
 
@@ -429,8 +462,12 @@ __global__ __launch_bounds__(kF8Threads, 2) void fwd_fp8_kernel(
     int hg, int H, int G) {
   using F = FwdF8<D, CAUSAL>;
   using C = F8Cfg<D>;
-  __shared__ __attribute__((aligned(1024))) unsigned char k_lds0[C::kTile];
-  __shared__ __attribute__((aligned(1024))) unsigned char k_lds1[C::kTile];
+  // a K buffer also holds the tile's K and V scale words (256 bytes each)
+  // after the codes: the compiler tracks in-flight LDS-DMA per LDS array
+  // for a few arrays only, and with more it waits for every load in flight
+  // before each read of LDS
+  __shared__ __attribute__((aligned(1024))) unsigned char k_lds0[C::kTile + 512];
+  __shared__ __attribute__((aligned(1024))) unsigned char k_lds1[C::kTile + 512];
   __shared__ __attribute__((aligned(1024))) unsigned char v_lds0[C::vTile];
   __shared__ __attribute__((aligned(1024))) unsigned char v_lds1[C::vTile];
   constexpr int BR = 32 * kF8Waves;
@@ -447,16 +484,24 @@ __global__ __launch_bounds__(kF8Threads, 2) void fwd_fp8_kernel(
   f.kbuf[1] = k_lds1;
   f.vbuf[0] = v_lds0;
   f.vbuf[1] = v_lds1;
+  f.ksbuf[0] = k_lds0 + C::kTile;
+  f.ksbuf[1] = k_lds1 + C::kTile;
+  f.vsbuf[0] = k_lds0 + C::kTile + 256;
+  f.vsbuf[1] = k_lds1 + C::kTile + 256;
   // K/V head of this query head (G query heads share one)
   const int64_t kvh = (int64_t)(bh / H) * (H / G) + (bh % H) / G;
   f.kh = k8 + kvh * N * D;
   f.ksh = ks + kvh * N * (D / 32);
   f.vth = v8t + kvh * T * D * kF8Keys;
   f.vsh = vs + kvh * T * 2 * 32 * (D / 32);
+  f.vs_bytes = T * 64 * (D / 32);
   f.N = N;
   f.wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   f.l32 = lane & 31;
   f.hl = lane >> 5;
+  // byte 0 of the K scale operand: block hl of the row; byte 1 (d = 128):
+  // block 2 + hl; the rest zero (selector 0x0c)
+  f.ksel = D == 128 ? (f.hl ? 0x0c0c0301u : 0x0c0c0200u) : (f.hl ? 0x0c0c0c01u : 0x0c0c0c00u);
   f.qw = q0 + 32 * f.wave;
   f.qi = f.qw + f.l32;
   f.c = scale * kLog2e;
