@@ -219,7 +219,11 @@ struct BwdQ {
     const int k0 = j * kRows;
     if (j + 1 < t_end) issue<PAR ^ 1>(k0 + kRows);
     if (!MASK || !CAUSAL || k0 <= wlast) consume<MASK, PAR>(k0);
-    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+    // The waits are the builtin, not inline assembly: the compiler then knows
+    // that the loads before them have landed and does not wait for them again
+    // (such a wait, placed after the next tile's loads were queued, would wait
+    // for those too).
+    __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0)
     __builtin_amdgcn_s_barrier();
   }
 };
@@ -297,7 +301,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(
   const int wlast = qw + 31;   // last query of the wave (causal skip)
 
   f.template issue<0>(0);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0)
   __syncthreads();
   int j = 0;
   const int full_end = min(n_tiles, n_full);
@@ -335,25 +339,33 @@ struct BwdKV {
   Dma<D, STR> qd;
   Dma<D, STR> gd;
   int q_rd, t_rd;
-  float stat;             // waves 0 and 1: the LSE*log2(e) or D of row `lane` of the next tile
+  float stat;             // waves 0 and 1: the LSE or D of row `lane` of the next tile (0 past N)
   unsigned char* qbuf[2];
   unsigned char* gbuf[2];
   float* lbuf[2];
   float* dbuf[2];
 
-  // Queue tile q0 (Q, dO by LDS-DMA; LSE and D into registers of waves 0, 1).
+  // Queue tile q0: LSE and D into registers of waves 0 and 1 first (range-
+  // checked, so rows past N read 0, and left untouched until publish, so
+  // that nothing waits for them before the step's closing wait), then Q and
+  // dO by LDS-DMA.
   template <int B>
   __device__ void issue(int q0) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    if (wave < 2) {
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)((wave == 0 ? lseh : dh) + q0), (short)0, (N - q0) * 4, 0x00020000);
+      stat = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, 4 * lane, 0, 0));
+    }
+#endif
     qd.issue(qh, q0, N, qbuf[B], wave);
     gd.issue(gh, q0, N, gbuf[B], wave);
-    const int r = q0 + lane;
-    if (wave == 0) stat = r < N ? lseh[r] * kLog2e : INFINITY;   // rows >= N get P = 0
-    else if (wave == 1) stat = r < N ? dh[r] : 0.f;
   }
-  // After the tile's loads have landed: make its row statistics visible.
+  // After the loads of tile q0 have landed: make its row statistics visible
+  // (LSE scaled by log2(e); rows >= N get LSE = +inf, hence P = 0, and D = 0).
   template <int B>
-  __device__ void publish() {
-    if (wave == 0) lbuf[B][lane] = stat;
+  __device__ void publish(int q0) {
+    if (wave == 0) lbuf[B][lane] = q0 + lane < N ? stat * kLog2e : INFINITY;
     else if (wave == 1) dbuf[B][lane] = stat;
   }
 
@@ -434,9 +446,9 @@ struct BwdKV {
   __device__ void step(int j, int next, bool has_next) {
     if (has_next) issue<PAR ^ 1>(next * kRows);
     consume<MASK, PAR>(j * kRows);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    if (has_next) publish<PAR ^ 1>();
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0)
+    if (has_next) publish<PAR ^ 1>(next * kRows);
+    __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0)
     __builtin_amdgcn_s_barrier();
   }
 };
@@ -514,9 +526,9 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dkdv_kernel(
 
   if (t0 < t1) {
     f.template issue<0>((t1 - 1) * kRows);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    f.template publish<0>();
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0)
+    f.template publish<0>((t1 - 1) * kRows);
+    __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0)
     __syncthreads();
     int j = t1 - 1;
     for (; j - 1 >= t_full; j -= 2) {

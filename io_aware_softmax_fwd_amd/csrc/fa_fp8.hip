@@ -440,7 +440,10 @@ struct FwdF8 {
     const int k0 = j * kF8Keys;
     if (j + 1 < t_end) issue<PAR ^ 1>(k0 + kF8Keys);
     if (!MASK || !CAUSAL || k0 <= qw + 31) consume<MASK, PAR>(k0);
-    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+    // the builtin wait (vmcnt(0) lgkmcnt(0)), which the compiler sees: it
+    // then does not wait for these loads again after the next tile's are
+    // queued
+    __builtin_amdgcn_s_waitcnt(0x0070u);
     __builtin_amdgcn_s_barrier();
     // A VALU read of a v_mfma_scale_f32_32x32x64_f8f6f4 result needs 20 wait
     // states on the MI355X (measured: at 19 the last result registers still
@@ -558,7 +561,7 @@ __global__ __launch_bounds__(kF8Threads, 2) void fwd_fp8_kernel(
   const int n_full = CAUSAL ? min(q0 + 1, N) / kF8Keys : N / kF8Keys;
 
   f.template issue<0>(0);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0x0F70u);   // vmcnt(0)
   __syncthreads();
   int j = 0;
   const int full_end = min(n_tiles, n_full);

@@ -64,6 +64,12 @@ namespace {
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
+// s_waitcnt immediates (gfx9 layout: vmcnt in bits 3:0 and 15:14, expcnt in
+// 6:4, lgkmcnt in 11:8; a field at its maximum does not wait)
+constexpr unsigned wait_vm(int n) { return 0x0F70u | (unsigned)(n & 15) | ((unsigned)(n >> 4) & 3u) << 14; }
+constexpr unsigned kWaitVm0 = wait_vm(0);
+constexpr unsigned kWaitLgkm0 = 0xC07Fu;
+constexpr unsigned kWaitVm0Lgkm0 = 0x0070u;
 constexpr int kKeys = 64;                 // keys per K/V tile (Bc)
 // A tile's probabilities against a stale offset are kept while every lane's
 // share of their sum (32 of them) is at most this, so no kept probability
@@ -307,7 +313,10 @@ struct Fwd {
     // nothing to do here or later; key chunks of a decoding step leave whole
     // waves without a query row.  The barrier below stays unconditional.
     if ((!SPLIT || rows) && (!MASK || !CAUSAL || k0 <= wlast)) consume<MASK, PAR, FIRST>(k0);
-    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+    // The builtin wait, not inline assembly: the compiler then knows that
+    // every load before it has landed, and does not wait for them again
+    // after the next tile's loads are queued (which would wait for those too).
+    __builtin_amdgcn_s_waitcnt(kWaitVm0Lgkm0);
     __builtin_amdgcn_s_barrier();
   }
 };
@@ -426,7 +435,7 @@ __global__ __launch_bounds__(kThreads, (QB == 1 || D == 64) ? 2 : 1) void fwd_bf
   if (t0 < t1) {
     f.template issue<false, 0>(t0 * kKeys);
     f.template issue<true, 0>(t0 * kKeys);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
     __syncthreads();
     // buffer parity counts from t0.  The first tile goes straight to the
     // row max (the offset is still -inf), skipping the probability pass that
@@ -617,16 +626,16 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void fwd_bf16_ws_kernel(
     const int jn = j + kWaves;
     const bool more = jn < n_tiles;
     f32x16 s[1][F::KB];
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(vDma) : "memory");
+    __builtin_amdgcn_s_waitcnt(wait_vm(vDma));
     f.scores(kt, s);
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
     if (more) load_k(jn * kKeys);
     bf16x8 pf[1][F::PS];
     f.template softmax<MASK, FIRST>(0, s[0], pf[0], j * kKeys);
-    if (more) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kDma) : "memory");
-    else      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    if (more) __builtin_amdgcn_s_waitcnt(wait_vm(kDma));
+    else      __builtin_amdgcn_s_waitcnt(kWaitVm0);
     f.pv(vt, pf);
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
     if (more) load_v(jn * kKeys);
   };
   constexpr int kPrefetch = 2;
@@ -661,7 +670,7 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void fwd_bf16_ws_kernel(
     for (int i = 0; i < kPrefetch; ++i) x ^= warm[i];
     asm volatile("" ::"v"(x));
   }
-  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(kWaitVm0Lgkm0);
   __syncthreads();
 
   // Partial results to LDS: the unnormalised O^T of the wave as fp32
