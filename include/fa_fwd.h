@@ -64,8 +64,9 @@ enum fa_status {
  *   lse     : device pointer, [B,H,N] float32, written.
  *   B, H, N : batch, heads, sequence length (N >= 1; any N, no tile multiple
  *             needed).  B*H*N*d must stay below 2^40 elements,
- *             B*H*ceil(N/32) (a bound of the workgroup count) below 2^31
- *             and one head (N*d elements) below 2 GiB.
+ *             B*H*ceil(N/32) below 2^24 (no launch may exceed 2^32
+ *             threads, the dispatch limit; 256 threads serve at most 32
+ *             rows) and one head (N*d elements) below 2 GiB.
  *   d       : head dimension, 64 or 128.
  *   scale   : multiplier of Q K^T before the softmax, finite and > 0
  *             (usually 1/sqrt(d)).
@@ -113,8 +114,9 @@ int fa_fwd_f32(const float* q, const float* k, const float* v, float* o,
  *               other argument; its contents are scratch (nothing is kept
  *               between calls, and calls sharing one workspace must not run
  *               concurrently).
- * Errors as for fa_fwd, plus FA_ERR_SHAPE for causal with Nq > Nk,
- * FA_ERR_SPLITS and FA_ERR_WORKSPACE.  With num_splits > 1 two kernels are
+ * Errors as for fa_fwd, plus FA_ERR_SHAPE for causal with Nq > Nk or when
+ * num_splits * B * H * ceil(Nq/128) reaches 2^24 (the key-split launch runs
+ * that many 256-thread workgroups), FA_ERR_SPLITS and FA_ERR_WORKSPACE.  With num_splits > 1 two kernels are
  * queued on `stream`; with num_splits == 1 the single-pass kernel writes O
  * and LSE directly (the workspace is still required and left untouched).
  */
@@ -183,7 +185,8 @@ size_t fa_fwd_splitkv_noalloc_max_bytes(void);
  * blocks (decoding) are packed into one tile, so K/V is read once per K/V
  * head rather than once per query head.  Results equal those of fa_fwd_splitkv
  * on K/V with every head repeated H/Hkv times, up to rounding order.
- * Errors as for fa_fwd_splitkv, plus FA_ERR_HEADS.
+ * Errors as for fa_fwd_splitkv (its workgroup bound counts the 128-row
+ * query tiles of each K/V head's packed rows), plus FA_ERR_HEADS.
  */
 int fa_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse,
                int B, int H, int Hkv, int Nq, int Nk, int d, float scale, int causal,
@@ -263,7 +266,8 @@ size_t fa_bwd_gqa_workspace_size(int B, int H, int Hkv, int N, int d);
  *
  * fa_quantize_qk_fp8: Q or K rows.  x bf16 [rows, d] (device) -> x8 codes
  *   [rows, d] (one byte each) and xs scales [rows, d/32] (block c covers
- *   dims 32c .. 32c+31).  rows >= 1, d in {64, 128}.
+ *   dims 32c .. 32c+31).  rows >= 1, d in {64, 128}, rows * d/32 below
+ *   2^32 (one thread per block).
  * fa_quantize_v_fp8: V of BH = B*H heads.  v bf16 [BH, N, d] -> v8t codes in
  *   fa_fp8_v_bytes(BH, N, d) bytes and vs scales in
  *   fa_fp8_v_scale_bytes(BH, N, d) bytes.  Blocks are 32 consecutive keys of
@@ -272,7 +276,7 @@ size_t fa_bwd_gqa_workspace_size(int B, int H, int Hkv, int N, int d);
  *   32h + j (h in {0,1}, j in 0..31) of a tile row holding key
  *   32*(j/16) + (j%4) + 8*((j%16)/4) + 4h of the tile; vs is [BH, T, 2, 32,
  *   d/32], element (t, b, i, c) the scale of keys 64t + 32b .. +31 of head
- *   dim 32c + i.
+ *   dim 32c + i.  BH * T * 2d must stay below 2^32 (threads of the launch).
  * fa_fwd_fp8: attention of the dequantized inputs.  q8, qs, k8, ks as
  *   written by fa_quantize_qk_fp8 for the [B*H*N, d] rows of Q and K; v8t,
  *   vs by fa_quantize_v_fp8 for V; o bf16 [B,H,N,d] and lse fp32 [B,H,N]

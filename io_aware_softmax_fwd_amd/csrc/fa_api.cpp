@@ -15,18 +15,19 @@
 
 namespace {
 
-// Largest supported problem: element offsets stay far inside int64 and the
-// 1-D grid (query tiles x heads) inside 2^31 workgroups.
+// Largest supported problem: element offsets stay far inside int64.
 constexpr int64_t kMaxElems = int64_t(1) << 40;
 constexpr int kMaxSplits = 256;
+// A dispatch carries its size in 32-bit work-item counts, so every launch
+// must stay below 2^32 threads: 2^24 workgroups of 256 threads.
+constexpr int64_t kMaxWorkgroups = int64_t(1) << 24;
 
 bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
 
 // Workgroup count bound of the square problems: no launch takes more than
-// one workgroup per 32 query rows of a head, and the kernels index heads and
-// workgroups with 32-bit integers.
+// one 256-thread workgroup per 32 query rows (or keys) of a head.
 bool grid_too_large(int64_t heads, int64_t rows_per_head) {
-  return heads * ((rows_per_head + 31) / 32) >= (int64_t(1) << 31);
+  return heads * ((rows_per_head + 31) / 32) >= kMaxWorkgroups;
 }
 
 bool overlap(const void* a, int64_t a_bytes, const void* b, int64_t b_bytes) {
@@ -78,7 +79,10 @@ int validate_gqa(const void* q, const void* k, const void* v, const void* o, con
   if (causal && Nq > Nk) return FA_ERR_SHAPE;
   if (splits < 1 || splits > kMaxSplits) return FA_ERR_SPLITS;
   const fa::QueryTiling t = fa::query_tiling(H / Hkv, Nq, causal);
-  if (t.n_qtiles * splits * B * Hkv >= (int64_t(1) << 31)) return FA_ERR_SHAPE;
+  // every launch of the call: at most this many 256-thread workgroups
+  // (the 32-row kernel for small grids runs only when the 128-row grid is
+  // under 192 workgroups)
+  if (t.n_qtiles * splits * B * Hkv >= kMaxWorkgroups) return FA_ERR_SHAPE;
   // the merge's 1-D grid: one thread per (query row, 8 head dims)
   if (splits > 1 && qrows * (d / 8) >= (int64_t(1) << 31)) return FA_ERR_SHAPE;
   if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(o) || misaligned(lse))
@@ -276,7 +280,8 @@ int fa_quantize_qk_fp8(const void* x, int64_t rows, int d, void* x8, void* xs, h
   if (!x || !x8 || !xs) return FA_ERR_NULL;
   if (rows < 1) return FA_ERR_SHAPE;
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED_D;
-  if (rows * d >= kMaxElems) return FA_ERR_SHAPE;
+  // one thread per 32-element block: below 2^32 threads
+  if (rows * d >= kMaxElems || rows * (d / 32) >= kMaxWorkgroups * 256) return FA_ERR_SHAPE;
   if (any_misaligned({x, x8, xs})) return FA_ERR_ALIGN;
   const int64_t xb = rows * d * 2, cb = rows * d, sb = rows * (d / 32);
   if (any_overlap(x8, cb, {{x, xb}, {xs, sb}}) || any_overlap(xs, sb, {{x, xb}})) return FA_ERR_ALIAS;
@@ -288,7 +293,8 @@ int fa_quantize_qk_fp8_rotated(const void* x, int64_t rows, int d, const signed 
   if (!x || !x8 || !xs) return FA_ERR_NULL;
   if (rows < 1) return FA_ERR_SHAPE;
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED_D;
-  if (rows * d >= kMaxElems) return FA_ERR_SHAPE;
+  // one thread per 32-element block: below 2^32 threads
+  if (rows * d >= kMaxElems || rows * (d / 32) >= kMaxWorkgroups * 256) return FA_ERR_SHAPE;
   if (any_misaligned({x, x8, xs})) return FA_ERR_ALIGN;
   const int64_t xb = rows * d * 2, cb = rows * d, sb = rows * (d / 32);
   if (any_overlap(x8, cb, {{x, xb}, {xs, sb}}) || any_overlap(xs, sb, {{x, xb}})) return FA_ERR_ALIAS;
@@ -311,6 +317,8 @@ int fa_quantize_v_fp8(const void* v, int BH, int N, int d, void* v8t, void* vs, 
   if (BH < 1 || N < 1) return FA_ERR_SHAPE;
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED_D;
   if ((int64_t)BH * N * d >= kMaxElems || (int64_t)N * d * 2 >= (int64_t(1) << 31)) return FA_ERR_SHAPE;
+  // 2d threads per 64-key block: below 2^32 threads
+  if ((int64_t)BH * ((N + 63) / 64) * 2 * d >= kMaxWorkgroups * 256) return FA_ERR_SHAPE;
   if (any_misaligned({v, v8t, vs})) return FA_ERR_ALIGN;
   const int64_t vb = (int64_t)BH * N * d * 2, cb = fa::fp8_v_code_bytes(BH, N, d),
                 sb = fa::fp8_v_scale_bytes(BH, N, d);
@@ -351,7 +359,7 @@ const char* fa_strerror(int status) {
   switch (status) {
     case FA_OK: return "success";
     case FA_ERR_NULL: return "a required pointer is NULL";
-    case FA_ERR_SHAPE: return "B, H, N must be >= 1, B*H*N*d below 2^40, B*H*ceil(N/32) below 2^31 and one head below 2 GiB";
+    case FA_ERR_SHAPE: return "B, H, N must be >= 1, B*H*N*d below 2^40, B*H*ceil(N/32) below 2^24 and one head below 2 GiB";
     case FA_ERR_UNSUPPORTED_D: return "head dimension must be 64 or 128";
     case FA_ERR_SCALE: return "scale must be finite and > 0";
     case FA_ERR_ALIGN: return "pointers must be 16-byte aligned";

@@ -63,6 +63,9 @@ def _call(fn, **kw):
     # 2^31 heads of one row: 2^37 elements, but one workgroup per head
     (dict(B=1 << 16, H=1 << 15, N=1, d=64), fa.FA_ERR_SHAPE),
     (dict(B=1 << 16, H=1 << 15, N=7, d=64), fa.FA_ERR_SHAPE),
+    # 2^24 groups of 32 rows: a launch would exceed 2^32 threads
+    (dict(B=1, H=1 << 14, N=1 << 15, d=64), fa.FA_ERR_SHAPE),
+    (dict(B=2, H=1 << 13, N=(1 << 15) - 31, d=64), fa.FA_ERR_SHAPE),
     (dict(d=32), fa.FA_ERR_UNSUPPORTED_D), (dict(d=96), fa.FA_ERR_UNSUPPORTED_D),
     (dict(d=256), fa.FA_ERR_UNSUPPORTED_D),
     (dict(scale=0.0), fa.FA_ERR_SCALE), (dict(scale=-0.5), fa.FA_ERR_SCALE),
@@ -110,6 +113,8 @@ def _split_call(**kw):
     (dict(q=None), fa.FA_ERR_NULL), (dict(lse=None), fa.FA_ERR_NULL),
     (dict(Nq=0), fa.FA_ERR_SHAPE), (dict(Nk=0), fa.FA_ERR_SHAPE),
     (dict(causal=1, Nq=129, Nk=128), fa.FA_ERR_SHAPE),
+    # 256 chunks x 1024 heads x 64 query tiles = 2^24 workgroups of 256 threads
+    (dict(H=1 << 10, Nq=1 << 13, Nk=1 << 13, splits=256), fa.FA_ERR_SHAPE),
     (dict(d=80), fa.FA_ERR_UNSUPPORTED_D), (dict(scale=-1.0), fa.FA_ERR_SCALE),
     (dict(causal=3), fa.FA_ERR_CAUSAL),
     (dict(splits=0), fa.FA_ERR_SPLITS), (dict(splits=257), fa.FA_ERR_SPLITS),
@@ -222,6 +227,7 @@ def _bwd_call(**kw):
     (dict(dq=A), fa.FA_ERR_ALIAS), (dict(dk=A + 48 * MB), fa.FA_ERR_ALIAS),
     (dict(dv=A + 40 * MB), fa.FA_ERR_ALIAS), (dict(ws=A + 64 * MB), fa.FA_ERR_ALIAS),
     (dict(dq=A + 32 * MB + 64), fa.FA_ERR_ALIAS),
+    (dict(H=1 << 14, N=1 << 15), fa.FA_ERR_SHAPE),
 ])
 def test_bwd_bad_arguments_rejected_on_host(kw, status):
     assert _bwd_call(**kw) == status
@@ -237,6 +243,7 @@ def test_bwd_workspace_size():
 @pytest.mark.parametrize("kw,status", [
     (dict(x=None), fa.FA_ERR_NULL), (dict(xs=None), fa.FA_ERR_NULL), (dict(rows=0), fa.FA_ERR_SHAPE),
     (dict(d=96), fa.FA_ERR_UNSUPPORTED_D), (dict(x8=A + 8 * MB + 4), fa.FA_ERR_ALIGN),
+    (dict(rows=1 << 30, d=128), fa.FA_ERR_SHAPE), (dict(rows=1 << 31, d=64), fa.FA_ERR_SHAPE),
     (dict(x8=A + 64), fa.FA_ERR_ALIAS), (dict(xs=A + 8 * MB + 128), fa.FA_ERR_ALIAS),
 ])
 def test_quantize_qk_fp8_bad_arguments(kw, status):
@@ -249,6 +256,8 @@ def test_quantize_qk_fp8_bad_arguments(kw, status):
     (dict(v=None), fa.FA_ERR_NULL), (dict(vs=None), fa.FA_ERR_NULL), (dict(BH=0), fa.FA_ERR_SHAPE),
     (dict(N=0), fa.FA_ERR_SHAPE), (dict(d=32), fa.FA_ERR_UNSUPPORTED_D),
     (dict(vs=A + 16 * MB + 2), fa.FA_ERR_ALIGN), (dict(v8t=A + 32), fa.FA_ERR_ALIAS),
+    # 2^14 heads x 2^10 tiles x 256 threads = 2^32 threads
+    (dict(BH=1 << 14, N=1 << 16), fa.FA_ERR_SHAPE),
 ])
 def test_quantize_v_fp8_bad_arguments(kw, status):
     a = dict(v=A, BH=2, N=100, d=128, v8t=A + 8 * MB, vs=A + 16 * MB, stream=None)
