@@ -10,8 +10,15 @@ it again): with fewer, the read returns the old value.
 
 The compiler inserts these wait states itself, but for the scaled fp8
 product it allows 19 on some control-flow paths, one fewer than the
-hardware needs.  This checker walks every path of a compiled kernel from
-each MFMA and reports reads that come too early.
+hardware needs.  check() walks every path of a compiled kernel from each
+MFMA and reports reads that come too early.
+
+prefetch_waits() looks for a performance fault of the same compiled code: a
+memory-counter wait that holds the matrix cores until the LDS-DMA loads of
+the next tile have landed.  A double-buffered tile loop queues those loads
+and then computes on the tile loaded before; a wait placed between the two
+(the compiler adds one when it cannot see that an earlier wait already
+covered the loads the products read) turns the prefetch into a stall.
 """
 import re
 
@@ -136,4 +143,43 @@ def check(ins, labels):
                 live = live - _writes(o, a)
             for s in _successors(j, ins, labels):
                 stack.append((s, nxt, live))
+    return found
+
+
+_VMEM_PREFIXES = ("buffer_", "global_", "scratch_", "flat_")
+
+
+def prefetch_waits(ins, min_products=8):
+    """Waits that force LDS-DMA loads queued since the last full memory wait
+    to complete and are followed by at least `min_products` MFMAs before the
+    next barrier, branch or end: a list of (wait index, products).
+
+    The scan is linear.  On gfx9 every vector-memory instruction (loads,
+    stores, scratch accesses) counts in vmcnt and completes in order, so
+    s_waitcnt vmcnt(n) completes all but the last n of them.
+    """
+    found = []
+    pending = []          # vector-memory ops since the last vmcnt(0): True = LDS DMA
+    for i, line in enumerate(ins):
+        op, ops = _split(line)
+        if op.startswith(_VMEM_PREFIXES):
+            pending.append(op.startswith("buffer_load") and bool(ops) and ops[-1].endswith("lds"))
+            continue
+        if op != "s_waitcnt":
+            continue
+        m = re.search(r"vmcnt\((\d+)\)", line)
+        if not m:
+            continue
+        done = pending[:max(0, len(pending) - int(m.group(1)))]
+        if any(done):
+            products = 0
+            for later in ins[i + 1:]:
+                o = later.split()[0]
+                if o in ("s_barrier", "s_branch", "s_endpgm") or o.startswith("s_cbranch"):
+                    break
+                if o.startswith("v_mfma"):
+                    products += 1
+            if products >= min_products:
+                found.append((i, products))
+        pending = pending[len(done):]
     return found

@@ -8,6 +8,10 @@ scaled product 20, bf16 product 12; tests/test_mfma_wait_states_gpu.py
 measures them again).  The compiler allows 19 after the fp8 product on some
 paths, so this is checked on the code as compiled, for every kernel of the
 library.
+
+The same compiled code is also checked for waits that hold the matrix cores
+until the next tile's LDS-DMA loads have landed (mfma_hazards.prefetch_waits):
+in a double-buffered tile loop such a wait turns the prefetch into a stall.
 """
 import os
 import subprocess
@@ -63,22 +67,77 @@ def _assembly(src, out):
     return subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True)
 
 
-def test_compiled_kernels_have_no_early_result_reads():
+@pytest.fixture(scope="module")
+def compiled():
+    """{(source, kernel symbol): (instructions, labels)} of the library's
+    three kernel sources, compiled to gfx950 assembly once."""
     from io_aware_softmax_fwd_amd import build as B
     if not os.path.exists(B.HIPCC):
         pytest.skip("hipcc not available")
     sources = ["fa_fwd_bf16.hip", "fa_bwd_bf16.hip", "fa_fp8.hip"]
+    kernels = {}
     with tempfile.TemporaryDirectory() as tmp:
-        procs = [(s, os.path.join(tmp, s + ".s")) for s in sources]
-        running = [(s, out, _assembly(s, out)) for s, out in procs]
-        problems, kernels = [], 0
+        running = [(s, os.path.join(tmp, s + ".s")) for s in sources]
+        running = [(s, out, _assembly(s, out)) for s, out in running]
         for s, out, p in running:
             _, err = p.communicate()
             assert p.returncode == 0, "hipcc -S %s failed:\n%s" % (s, err)
-            for name, (ins, labels) in H.parse_kernels(open(out).read()).items():
-                kernels += 1
-                for i, j, st in H.check(ins, labels):
-                    problems.append("%s %s: '%s' read after %d wait states by '%s'"
-                                    % (s, name[:60], ins[i][:60], st, ins[j][:60]))
-    assert kernels >= 20
+            for name, parsed in H.parse_kernels(open(out).read()).items():
+                kernels[(s, name)] = parsed
+    return kernels
+
+
+def test_compiled_kernels_have_no_early_result_reads(compiled):
+    problems = []
+    for (s, name), (ins, labels) in compiled.items():
+        for i, j, st in H.check(ins, labels):
+            problems.append("%s %s: '%s' read after %d wait states by '%s'"
+                            % (s, name[:60], ins[i][:60], st, ins[j][:60]))
+    assert len(compiled) >= 20
+    assert not problems, "\n".join(problems)
+
+
+DMA = "buffer_load_dwordx4 v1, s[4:7], 0 offen lds"
+BF16 = "v_mfma_f32_32x32x16_bf16 v[0:15], v[16:19], v[20:23], v[0:15]"
+
+
+def test_prefetch_wait_checker():
+    eight = "\n".join([BF16] * 8)
+    # a full wait right after queuing the next tile, before the products
+    ins, _ = _kernel("\n".join([DMA, "s_waitcnt vmcnt(0)", eight, "s_barrier", "s_endpgm"]))
+    assert H.prefetch_waits(ins) == [(1, 8)]
+    # the same wait after the products costs nothing
+    ins, _ = _kernel("\n".join([DMA, eight, "s_waitcnt vmcnt(0)", "s_barrier", "s_endpgm"]))
+    assert H.prefetch_waits(ins) == []
+    # a wait that completes only an older load (loads complete in order)
+    ins, _ = _kernel("\n".join(["buffer_load_dword v2, v3, s[4:7], 0 offen", DMA,
+                                 "s_waitcnt vmcnt(1)", eight, "s_endpgm"]))
+    assert H.prefetch_waits(ins) == []
+    # ... but not a newer one queued after the DMA
+    ins, _ = _kernel("\n".join([DMA, "buffer_load_dword v2, v3, s[4:7], 0 offen",
+                                 "s_waitcnt vmcnt(0)", eight, "s_endpgm"]))
+    assert H.prefetch_waits(ins) == [(2, 8)]
+    # fewer products than the threshold before the barrier
+    ins, _ = _kernel("\n".join([DMA, "s_waitcnt vmcnt(0)", BF16, "s_barrier", eight, "s_endpgm"]))
+    assert H.prefetch_waits(ins) == []
+
+
+# Double-buffered tile loops, which queue the next tile's K/V and then
+# compute on the current one.  Left out: the forward for small grids (one
+# K and one V slot per wave, refilled as soon as each is read, so its waits
+# are the pipeline) and the causal dK/dV kernel, whose loop over the
+# diagonal query tiles reloads spilled registers from scratch.
+_DOUBLE_BUFFERED = ("fwd_bf16_kernel", "fwd_fp8_kernel", "bwd_dq_kernel",
+                    "bwd_dkdv_kernelILi64ELb0", "bwd_dkdv_kernelILi128ELb0")
+
+
+def test_tile_loops_do_not_wait_for_their_prefetch(compiled):
+    checked, problems = 0, []
+    for (s, name), (ins, _) in compiled.items():
+        if not any(k in name for k in _DOUBLE_BUFFERED):
+            continue
+        checked += 1
+        for i, n in H.prefetch_waits(ins):
+            problems.append("%s %s: '%s' before %d products" % (s, name[:60], ins[i], n))
+    assert checked >= 16
     assert not problems, "\n".join(problems)
