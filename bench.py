@@ -78,14 +78,23 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fa_fwd_bf16_traffic.json")
 # the sources that decide the forward kernels' code and launch (the entry
 # points' argument checks in fa_api.cpp do not change what runs)
 KERNEL_SOURCES = ["fa_fwd_bf16.hip", "fa_fwd_f32.hip", "fa_device.h", "fa_internal.h"]
+# the same for the backward and fp8 kernels, whose summaries carry the hash
+# of their own sources
+BWD_SOURCES = ["fa_bwd_bf16.hip", "fa_device.h", "fa_internal.h"]
+FP8_SOURCES = ["fa_fp8.hip", "fa_device.h", "fa_internal.h"]
 
 
-def kernel_source_hash():
+def kernel_source_hash(names=None):
     h = hashlib.sha256()
-    for name in KERNEL_SOURCES:
+    for name in names or KERNEL_SOURCES:
         with open(os.path.join(ROOT, "io_aware_softmax_fwd_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
+
+
+def _source_note(names):
+    """'kernel source HASH of FILES' for a summary header."""
+    return "kernel source %s of %s" % (kernel_source_hash(names), ", ".join(names))
 
 
 def _traffic_table():
@@ -265,6 +274,10 @@ TRACE_ONLY = {"decode_gqa": "fa_fwd_gqa_decode_b1_h32_hkv8_nk131072_d128",
               "bwd": "fa_bwd_bf16_n16k_d128_causal_amplified",
               "fp8": "fa_fwd_fp8_bf16_n16k_d128_causal_amplified",
               "gqa": "fa_fwd_gqa_hkv8_bf16_n16k_d128_causal_amplified"}
+# sources whose hash a summary of another path carries (default: the
+# forward kernels')
+SUMMARY_SOURCES = {"fa_bwd_bf16_n16k_d128_causal_amplified": BWD_SOURCES,
+                   "fa_fwd_fp8_bf16_n16k_d128_causal_amplified": FP8_SOURCES}
 # counter steps of other paths, summarised kernel by kernel: summary name ->
 # (steps, kernel-name key)
 COUNTERS_ONLY = {"fa_bwd_bf16_n16k_d128_causal_amplified": (("bwd_sq", "bwd_sq2"), "fa::(anonymous namespace)::bwd_"),
@@ -409,7 +422,8 @@ def summarize(out_dir, workload_name, wl=4):
                 out.append("  derived: non-MFMA VALU instructions per MFMA = %.2f" % (
                     (c.get("SQ_INSTS_VALU", 0) - c["SQ_INSTS_MFMA"]) / c["SQ_INSTS_MFMA"]))
         with open(os.path.join(prof, "%s_counters.txt" % name), "w") as f:
-            f.write("# rocprofv3 counters per launch, per kernel, %s (kernel source %s)\n" % (name, src_hash))
+            f.write("# rocprofv3 counters per launch, per kernel, %s (%s)\n"
+                    % (name, _source_note(SUMMARY_SOURCES.get(name, KERNEL_SOURCES))))
             f.write("# commands:\n" + "".join("#   %s\n" % PROFILE_STEPS[p] for p in steps_))
             f.write("\n".join(out) + "\n")
     # kernel-only traces of other calls (every kernel of the call)
@@ -421,7 +435,7 @@ def summarize(out_dir, workload_name, wl=4):
             row["Name"], row["Calls"], float(row["AverageNs"]) / 1e3,
             float(row["MinNs"]) / 1e3, float(row["MaxNs"]) / 1e3) for row in st]
         with open(os.path.join(prof, "%s_kernel_trace.txt" % name), "w") as f:
-            f.write("# rocprofv3 kernel trace, %s (kernel source %s)\n" % (name, src_hash))
+            f.write("# rocprofv3 kernel trace, %s (%s)\n" % (name, _source_note(SUMMARY_SOURCES.get(name, KERNEL_SOURCES))))
             f.write("# command: %s\n" % PROFILE_STEPS[step])
             f.write("\n".join(out) + "\n")
     print(json.dumps({"kernel_avg_us": avg_ns / 1e3 if avg_ns else None,

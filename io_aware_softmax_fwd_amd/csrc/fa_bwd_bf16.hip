@@ -455,9 +455,9 @@ struct BwdKV {
 
 template <int D, bool CAUSAL>
 // Two workgroups per CU (2 x 77 KB of LDS at d = 128): 256 registers a
-// lane.  The causal variants then keep some values in scratch, but only in
-// the loop over the diagonal query tiles, which are a few of each
-// workgroup's tiles; the loop over the unmasked tiles stays in registers.
+// lane.  The causal d = 128 variant keeps a few values in scratch, reloaded
+// around its two masked steps (once per workgroup); the loop over the whole
+// tiles stays in registers.
 __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dkdv_kernel(
     const unsigned short* __restrict__ q, const unsigned short* __restrict__ k,
     const unsigned short* __restrict__ v, const unsigned short* __restrict__ dout,
@@ -518,31 +518,42 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dkdv_kernel(
   f.t_rd = tr_offset<F::STR>(lane);
 
   // Query tiles that see any of this workgroup's keys: [t0, t1).  Causal:
-  // tiles before t_full hold a query that precedes one of the keys and are
-  // masked; they are consumed last (the loop walks down from t1 - 1).
+  // the two tiles t0 and t0 + 1 cover the workgroup's own 128 positions and
+  // hold queries that precede some of its keys, so they are masked; every
+  // later tile is whole.  The masked pair goes first, from buffers 0 and 1,
+  // so that the whole tiles after it start on buffer 0 as well and every
+  // step's buffers are fixed at compile time (a buffer chosen at run time
+  // merges two copies of the step in one loop, which the compiler serves by
+  // spilling).  The whole tiles are walked down from t1 - 1, so the
+  // workgroups of a head sweep the same Q and dO tiles at about the same
+  // time.
+  static_assert(BK == 2 * kRows, "the diagonal of a workgroup spans two query tiles");
   const int t0 = CAUSAL ? k0 / kRows : 0;
   const int t1 = (N + kRows - 1) / kRows;
-  const int t_full = CAUSAL ? min(t1, (k0 + BK - 1 + kRows - 1) / kRows) : t0;
+  const int t_full = CAUSAL ? min(t1, t0 + 2) : t0;
 
   if (t0 < t1) {
-    f.template issue<0>((t1 - 1) * kRows);
+    const int first = CAUSAL ? t0 : t1 - 1;
+    f.template issue<0>(first * kRows);
     __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0)
-    f.template publish<0>((t1 - 1) * kRows);
+    f.template publish<0>(first * kRows);
     __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0)
     __syncthreads();
+    if constexpr (CAUSAL) {
+      // t0, then t0 + 1 if it exists; the whole tiles follow from t1 - 1
+      if (t0 + 1 < t1) {
+        f.template step<true, 0>(t0, t0 + 1, true);
+        f.template step<true, 1>(t0 + 1, t1 - 1, t1 - 1 >= t_full);
+      } else {
+        f.template step<true, 0>(t0, 0, false);
+      }
+    }
     int j = t1 - 1;
     for (; j - 1 >= t_full; j -= 2) {
       f.template step<false, 0>(j, j - 1, true);
-      f.template step<false, 1>(j - 1, j - 2, j - 2 >= t0);
+      f.template step<false, 1>(j - 1, j - 2, j - 2 >= t_full);
     }
-    if (j >= t_full) {
-      f.template step<false, 0>(j, j - 1, j - 1 >= t0);
-      --j;
-    }
-    for (; j >= t0; --j) {
-      if ((t1 - 1 - j) & 1) f.template step<true, 1>(j, j - 1, j - 1 >= t0);
-      else                  f.template step<true, 0>(j, j - 1, j - 1 >= t0);
-    }
+    if (j >= t_full) f.template step<false, 0>(j, 0, false);
   }
   if (valid) {
     if (G == 1) {

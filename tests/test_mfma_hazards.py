@@ -122,13 +122,14 @@ def test_prefetch_wait_checker():
     assert H.prefetch_waits(ins) == []
 
 
-# Double-buffered tile loops, which queue the next tile's K/V and then
-# compute on the current one.  Left out: the forward for small grids (one
-# K and one V slot per wave, refilled as soon as each is read, so its waits
-# are the pipeline) and the causal dK/dV kernel, whose loop over the
-# diagonal query tiles reloads spilled registers from scratch.
+# Double-buffered tile loops, which queue the next tile's K/V (or Q/dO) and
+# then compute on the current one.  Left out: the forward for small grids
+# (one K and one V slot per wave, refilled as soon as each is read, so its
+# waits are the pipeline) and the causal d = 128 dK/dV kernel, whose two
+# masked steps reload a few spilled registers from scratch (once per
+# workgroup) and wait for them, loads queued before included.
 _DOUBLE_BUFFERED = ("fwd_bf16_kernel", "fwd_fp8_kernel", "bwd_dq_kernel",
-                    "bwd_dkdv_kernelILi64ELb0", "bwd_dkdv_kernelILi128ELb0")
+                    "bwd_dkdv_kernelILi64E", "bwd_dkdv_kernelILi128ELb0")
 
 
 def test_tile_loops_do_not_wait_for_their_prefetch(compiled):
@@ -139,5 +140,5 @@ def test_tile_loops_do_not_wait_for_their_prefetch(compiled):
         checked += 1
         for i, n in H.prefetch_waits(ins):
             problems.append("%s %s: '%s' before %d products" % (s, name[:60], ins[i], n))
-    assert checked >= 16
+    assert checked >= 17
     assert not problems, "\n".join(problems)
