@@ -24,7 +24,10 @@
 //                    straight from the accumulators as B operands, with the
 //                    transposed operand read by ds_read_b64_tr_b16.
 // Both recompute S and dP: seven N^2 d products in all against five for a
-// single kernel that adds dQ with atomics, traded for determinism.
+// single kernel that adds dQ with atomics, traded for determinism.  When
+// neither grid alone would fill the GPU (at most 128 workgroups each), D is
+// written by a small row-dot kernel first and the two kernels' workgroups
+// run as one launch (bwd_fused_kernel), side by side.
 #include <math.h>
 
 #include "fa_device.h"
@@ -228,9 +231,31 @@ struct BwdQ {
   }
 };
 
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(
-    const unsigned short* __restrict__ q, const unsigned short* __restrict__ k,
+// D_i = <dO_i, O_i> of this lane's row: its 64 dims (half hl of the row),
+// then the other half-wave's.  The dQ kernel and the row-dot kernel share
+// it, so both produce the same bits.
+template <int D>
+__device__ __forceinline__ float row_dot(const unsigned short* orow, bool valid, int hl,
+                                         const bf16x8 (&gf)[D / 16]) {
+  bf16x8 of[D / 16];
+  load_row_fragments<D>(orow, valid, hl, of);
+  float part = 0.f;
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks)
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+      const bf16x2 a = {gf[ks][e], gf[ks][e + 1]};
+      const bf16x2 b = {of[ks][e], of[ks][e + 1]};
+      part = __builtin_amdgcn_fdot2_f32_bf16(a, b, part, false);
+    }
+  return sum_across_halves(part);
+}
+
+// One dQ workgroup (block `blk` of n_qtiles * BH).  WRITE_D: also store D
+// for the dK/dV kernel (the fused small-grid launch has it written first).
+template <int D, bool CAUSAL, bool WRITE_D>
+__device__ __forceinline__ void dq_block(
+    int blk, const unsigned short* __restrict__ q, const unsigned short* __restrict__ k,
     const unsigned short* __restrict__ v, const unsigned short* __restrict__ o,
     const unsigned short* __restrict__ dout, const float* __restrict__ lse,
     unsigned short* __restrict__ dq, float* __restrict__ dws, int N, int BH, int n_qtiles,
@@ -240,11 +265,11 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(
   __shared__ __attribute__((aligned(1024))) unsigned char k_lds1[Dma<D, F::KSTR>::bytes];
   __shared__ __attribute__((aligned(1024))) unsigned char v_lds0[Dma<D, F::VSTR>::bytes];
   __shared__ __attribute__((aligned(1024))) unsigned char v_lds1[Dma<D, F::VSTR>::bytes];
-  constexpr int KS = D / 16, DB = D / 32, BR = 32 * kBwdWaves;
+  constexpr int DB = D / 32, BR = 32 * kBwdWaves;
 
   const int tid = threadIdx.x, lane = tid & 63;
   int bh, rank;
-  xcd_order(blockIdx.x, BH, n_qtiles, hg, bh, rank);
+  xcd_order(blk, BH, n_qtiles, hg, bh, rank);
   const int qt = n_qtiles - 1 - rank;   // heaviest causal tiles first
   const int q0 = qt * BR;
   const int64_t head = (int64_t)bh * N * D;
@@ -268,23 +293,9 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(
   const unsigned short* qrow = q + head + (int64_t)f.qi * D;
   load_row_fragments<D>(qrow, valid, f.hl, f.qf);
   load_row_fragments<D>(dout + head + (int64_t)f.qi * D, valid, f.hl, f.gf);
-  {
-    // D_i = <dO_i, O_i>: this lane's 64 dims, then the other half-wave's
-    bf16x8 of[KS];
-    load_row_fragments<D>(o + head + (int64_t)f.qi * D, valid, f.hl, of);
-    float part = 0.f;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-      for (int e = 0; e < 8; e += 2) {
-        const bf16x2 a = {f.gf[ks][e], f.gf[ks][e + 1]};
-        const bf16x2 b = {of[ks][e], of[ks][e + 1]};
-        part = __builtin_amdgcn_fdot2_f32_bf16(a, b, part, false);
-      }
-    f.Drow = sum_across_halves(part);
-  }
+  f.Drow = row_dot<D>(o + head + (int64_t)f.qi * D, valid, f.hl, f.gf);
   f.lse2 = valid ? lse[(int64_t)bh * N + f.qi] * kLog2e : 0.f;
-  if (valid && f.hl == 0) dws[(int64_t)bh * N + f.qi] = f.Drow;
+  if (WRITE_D && valid && f.hl == 0) dws[(int64_t)bh * N + f.qi] = f.Drow;
 #pragma unroll
   for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -318,6 +329,16 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(
     else       f.template step<true, 0>(j, n_tiles, wlast);
   }
   if (valid) store_rowT<D>(dq + head + (int64_t)f.qi * D, f.acc, scale, f.hl);
+}
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(
+    const unsigned short* __restrict__ q, const unsigned short* __restrict__ k,
+    const unsigned short* __restrict__ v, const unsigned short* __restrict__ o,
+    const unsigned short* __restrict__ dout, const float* __restrict__ lse,
+    unsigned short* __restrict__ dq, float* __restrict__ dws, int N, int BH, int n_qtiles,
+    float scale, int hg, int H, int G) {
+  dq_block<D, CAUSAL, true>(blockIdx.x, q, k, v, o, dout, lse, dq, dws, N, BH, n_qtiles, scale, hg, H, G);
 }
 
 // ------------------------------------------------------------- dK/dV kernel
@@ -453,13 +474,10 @@ struct BwdKV {
   }
 };
 
+// One dK/dV workgroup (block `blk` of ceil(N/128) * BH).
 template <int D, bool CAUSAL>
-// Two workgroups per CU (2 x 77 KB of LDS at d = 128): 256 registers a
-// lane.  The causal d = 128 variant keeps a few values in scratch, reloaded
-// around its two masked steps (once per workgroup); the loop over the whole
-// tiles stays in registers.
-__global__ __launch_bounds__(kBwdThreads, 2) void bwd_dkdv_kernel(
-    const unsigned short* __restrict__ q, const unsigned short* __restrict__ k,
+__device__ __forceinline__ void dkdv_block(
+    int blk, const unsigned short* __restrict__ q, const unsigned short* __restrict__ k,
     const unsigned short* __restrict__ v, const unsigned short* __restrict__ dout,
     const float* __restrict__ lse, const float* __restrict__ dws, unsigned short* __restrict__ dk,
     unsigned short* __restrict__ dv, int N, int BH, float scale, int hg, int H, int G,
@@ -477,7 +495,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dkdv_kernel(
 
   const int tid = threadIdx.x, lane = tid & 63;
   int bh, kt;   // smallest keys first: they meet the most causal queries
-  xcd_order(blockIdx.x, BH, (N + BK - 1) / BK, hg, bh, kt);
+  xcd_order(blk, BH, (N + BK - 1) / BK, hg, bh, kt);
   const int k0 = kt * BK;
   const int64_t head = (int64_t)bh * N * D;
   const int64_t kvh = (int64_t)kv_head(bh, H, G) * N * D;
@@ -567,6 +585,54 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dkdv_kernel(
   }
 }
 
+// Two workgroups per CU (2 x 77 KB of LDS at d = 128): 256 registers a
+// lane.  The causal d = 128 variant keeps a few values in scratch, reloaded
+// around its two masked steps (once per workgroup); the loop over the whole
+// tiles stays in registers.
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kBwdThreads, 2) void bwd_dkdv_kernel(
+    const unsigned short* __restrict__ q, const unsigned short* __restrict__ k,
+    const unsigned short* __restrict__ v, const unsigned short* __restrict__ dout,
+    const float* __restrict__ lse, const float* __restrict__ dws, unsigned short* __restrict__ dk,
+    unsigned short* __restrict__ dv, int N, int BH, float scale, int hg, int H, int G,
+    float* __restrict__ pdk, float* __restrict__ pdv) {
+  dkdv_block<D, CAUSAL>(blockIdx.x, q, k, v, dout, lse, dws, dk, dv, N, BH, scale, hg, H, G, pdk, pdv);
+}
+
+// D_i = <dO_i, O_i> of every row into the workspace, for the fused launch
+// below (one wave per 32 rows, lanes as in the dQ kernel).
+template <int D>
+__global__ __launch_bounds__(kBwdThreads) void bwd_rowdot_kernel(const unsigned short* __restrict__ o,
+                                                                 const unsigned short* __restrict__ dout,
+                                                                 float* __restrict__ dws, int64_t rows) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = ((int64_t)blockIdx.x * kBwdWaves + (threadIdx.x >> 6)) * 32 + (lane & 31);
+  const bool valid = row < rows;
+  const int hl = lane >> 5;
+  bf16x8 gf[D / 16];
+  load_row_fragments<D>(dout + row * D, valid, hl, gf);
+  const float dr = row_dot<D>(o + row * D, valid, hl, gf);
+  if (valid && hl == 0) dws[row] = dr;
+}
+
+// Small grids: the dQ and the dK/dV workgroups in one launch (blocks below
+// n_dq take the dQ work), so that they run side by side when neither grid
+// alone fills the GPU.  D comes from bwd_rowdot_kernel, launched first.
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kBwdThreads, 1) void bwd_fused_kernel(
+    const unsigned short* __restrict__ q, const unsigned short* __restrict__ k,
+    const unsigned short* __restrict__ v, const unsigned short* __restrict__ o,
+    const unsigned short* __restrict__ dout, const float* __restrict__ lse,
+    unsigned short* __restrict__ dq, unsigned short* __restrict__ dk, unsigned short* __restrict__ dv,
+    float* __restrict__ dws, int N, int BH, int n_qtiles, float scale, int hg, int H, int G,
+    float* __restrict__ pdk, float* __restrict__ pdv) {
+  const int n_dq = n_qtiles * BH;
+  if ((int)blockIdx.x < n_dq)
+    dq_block<D, CAUSAL, false>(blockIdx.x, q, k, v, o, dout, lse, dq, dws, N, BH, n_qtiles, scale, hg, H, G);
+  else
+    dkdv_block<D, CAUSAL>(blockIdx.x - n_dq, q, k, v, dout, lse, dws, dk, dv, N, BH, scale, hg, H, G, pdk, pdv);
+}
+
 // dK and dV of each K/V head: the sum of its G query heads' fp32 shares, in
 // head order (a fixed order, so the result is reproducible), rounded to
 // bf16.  One thread per (K/V head row, 8 head dims).
@@ -598,6 +664,11 @@ __global__ __launch_bounds__(256) void bwd_group_sum_kernel(const float* __restr
   }
 }
 
+// Up to this many workgroups in all (the dQ and the dK/dV grids together,
+// one workgroup per CU of the 256 at the fused kernel's LDS use), the two
+// kernels run as one launch.
+constexpr int64_t kBwdFusedMaxGrid = 256;
+
 template <int D, bool CAUSAL>
 hipError_t launch_bwd(const BwdProblem& p, hipStream_t stream) {
   const int BH = p.B * p.H;
@@ -608,21 +679,31 @@ hipError_t launch_bwd(const BwdProblem& p, hipStream_t stream) {
   const unsigned short* k = static_cast<const unsigned short*>(p.k);
   const unsigned short* v = static_cast<const unsigned short*>(p.v);
   const unsigned short* dout = static_cast<const unsigned short*>(p.dout);
+  const unsigned short* o = static_cast<const unsigned short*>(p.o);
   float* dws = static_cast<float*>(p.workspace);
-  hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)((int64_t)n_qtiles * BH)),
-                     dim3(kBwdThreads), 0, stream, q, k, v,
-                     static_cast<const unsigned short*>(p.o), dout, p.lse,
-                     static_cast<unsigned short*>(p.dq), dws, p.N, BH, n_qtiles, p.scale, hg, p.H, G);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
   const BwdLayout L = bwd_layout(p.B, p.H, p.Hkv, p.N, D);
   unsigned char* ws = static_cast<unsigned char*>(p.workspace);
   float* pdk = G > 1 ? reinterpret_cast<float*>(ws + L.dk_offset) : nullptr;
   float* pdv = G > 1 ? reinterpret_cast<float*>(ws + L.dv_offset) : nullptr;
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)((int64_t)n_qtiles * BH)),
-                     dim3(kBwdThreads), 0, stream, q, k, v, dout, p.lse, dws,
-                     static_cast<unsigned short*>(p.dk), static_cast<unsigned short*>(p.dv), p.N, BH,
-                     p.scale, hg, p.H, G, pdk, pdv);
+  unsigned short* dq = static_cast<unsigned short*>(p.dq);
+  unsigned short* dk = static_cast<unsigned short*>(p.dk);
+  unsigned short* dv = static_cast<unsigned short*>(p.dv);
+  const int64_t grid = (int64_t)n_qtiles * BH;   // workgroups of each of the two kernels
+  hipError_t e;
+  if (2 * grid <= kBwdFusedMaxGrid) {
+    const int64_t rows = (int64_t)BH * p.N;
+    hipLaunchKernelGGL((bwd_rowdot_kernel<D>), dim3((unsigned)((rows + 32 * kBwdWaves - 1) / (32 * kBwdWaves))),
+                       dim3(kBwdThreads), 0, stream, o, dout, dws, rows);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL((bwd_fused_kernel<D, CAUSAL>), dim3((unsigned)(2 * grid)), dim3(kBwdThreads), 0, stream,
+                       q, k, v, o, dout, p.lse, dq, dk, dv, dws, p.N, BH, n_qtiles, p.scale, hg, p.H, G, pdk, pdv);
+  } else {
+    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)grid), dim3(kBwdThreads), 0, stream,
+                       q, k, v, o, dout, p.lse, dq, dws, p.N, BH, n_qtiles, p.scale, hg, p.H, G);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)grid), dim3(kBwdThreads), 0, stream,
+                       q, k, v, dout, p.lse, dws, dk, dv, p.N, BH, p.scale, hg, p.H, G, pdk, pdv);
+  }
   e = hipGetLastError();
   if (e != hipSuccess || G == 1) return e;
   const int64_t kv_rows = (int64_t)p.B * p.Hkv * p.N;

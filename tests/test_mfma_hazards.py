@@ -129,7 +129,7 @@ def test_prefetch_wait_checker():
 # masked steps reload a few spilled registers from scratch (once per
 # workgroup) and wait for them, loads queued before included.
 _DOUBLE_BUFFERED = ("fwd_bf16_kernel", "fwd_fp8_kernel", "bwd_dq_kernel",
-                    "bwd_dkdv_kernelILi64E", "bwd_dkdv_kernelILi128ELb0")
+                    "bwd_dkdv_kernelILi64E", "bwd_dkdv_kernelILi128ELb0", "bwd_fused_kernel")
 
 
 def test_tile_loops_do_not_wait_for_their_prefetch(compiled):
@@ -140,5 +140,5 @@ def test_tile_loops_do_not_wait_for_their_prefetch(compiled):
         checked += 1
         for i, n in H.prefetch_waits(ins):
             problems.append("%s %s: '%s' before %d products" % (s, name[:60], ins[i], n))
-    assert checked >= 17
+    assert checked >= 21
     assert not problems, "\n".join(problems)
