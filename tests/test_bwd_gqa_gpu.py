@@ -36,6 +36,10 @@ def _close(name, got, ref, case):
     (2, 4, 1, 200, 64, False),
     (1, 6, 3, 513, 64, True),
     (1, 16, 2, 129, 128, False),
+    # more than 128 query tiles of 128 rows: the two separate kernels (the
+    # cases above run as one fused launch)
+    (1, 144, 8, 130, 64, True),
+    (2, 72, 24, 200, 128, False),
 ])
 def test_bwd_gqa_matches_oracle(B, H, Hkv, N, d, causal):
     torch = torch_or_skip()
