@@ -404,8 +404,12 @@ def summarize(out_dir, workload_name, wl=4):
                             continue
                         kern = row["Kernel_Name"].replace("(anonymous namespace)::", "").split("(")[0]
                         kern = kern.replace("void ", "")
+                        # one reading per pass and dispatch (summed over the blocks
+                        # it lists); a counter that both passes collect
+                        # (GRBM_GUI_ACTIVE) is averaged over the passes
                         d = per_kernel.setdefault(kern, {}).setdefault(row["Counter_Name"], {})
-                        d[row["Dispatch_Id"]] = d.get(row["Dispatch_Id"], 0.0) + float(row["Counter_Value"])
+                        at = (part, row["Dispatch_Id"])
+                        d[at] = d.get(at, 0.0) + float(row["Counter_Value"])
         if not per_kernel:
             continue
         out = []

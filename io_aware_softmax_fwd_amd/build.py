@@ -23,6 +23,15 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 DEVICE_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
                 "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
                 "-Wall", "-Wno-unused-function"]
+# Per-source additions.  fa_fp8.hip is compiled without machine sinking:
+# it would move the next tile's score products of the d = 64 walk below the
+# offset test's branch, out of the stretch where they overlap the vector
+# work (the d = 128 walk also measured 2-3 % faster without it).
+SOURCE_FLAGS = {"fa_fp8.hip": ["-mllvm", "-disable-machine-sink"]}
+
+
+def device_flags(src: str) -> list:
+    return DEVICE_FLAGS + SOURCE_FLAGS.get(src, [])
 
 
 def build(verbose: bool = False) -> str:
@@ -32,7 +41,7 @@ def build(verbose: bool = False) -> str:
     procs = []
     for src in SOURCES:
         obj = os.path.join(bdir, src + ".o")
-        cmd = [HIPCC, *DEVICE_FLAGS, "-I", INCLUDE, "-I", CSRC, "-c",
+        cmd = [HIPCC, *device_flags(src), "-I", INCLUDE, "-I", CSRC, "-c",
                os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)

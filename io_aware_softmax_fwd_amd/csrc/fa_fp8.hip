@@ -33,6 +33,9 @@
 //   O^T += V^T P^T   v_mfma_scale 32x32x64 with the V block scales.
 // The fp8 matrix cores run at twice the bf16 rate, so a 64-key tile costs
 // nine 32x32x64 products per wave against thirty-two 32x32x16 in bf16.
+// d = 128 walks the tiles one per step; d = 64, whose vector work is about
+// twice its matrix work, keeps three tiles in flight per step so that the
+// two overlap within a wave (FwdF8::walk_pipelined).
 #include <math.h>
 
 #include "fa_device.h"
@@ -290,29 +293,19 @@ struct FwdF8 {
   unsigned char* vsbuf[2];
   unsigned char* ksbuf[2];
 
-  // Queue tile k0 into buffer B: K and V^T codes by LDS-DMA, scale words
-  // into registers.
+  // Queue the K tile at key k0 into buffer B: codes by LDS-DMA, scale words
+  // into LDS after the codes (d = 128) or into registers (d = 64).
   template <int B>
-  __device__ void issue(int k0) {
+  __device__ void issue_k(int k0) {
 #if defined(__HIP_DEVICE_COMPILE__)
     const __amdgpu_buffer_rsrc_t rk =
         __builtin_amdgcn_make_buffer_rsrc((void*)(kh + (int64_t)k0 * D), (short)0, (N - k0) * D, 0x00020000);
-    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(vth + (int64_t)(k0 / kF8Keys) * D * kF8Keys), (short)0, D * kF8Keys, 0x00020000);
 #pragma unroll
     for (int i = 0; i < C::kDmaPerWave; ++i) {
       const int blk = wave + kF8Waves * i;
       if (C::kDma % kF8Waves == 0 || blk < C::kDma)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(kbuf[B] + blk * 1024), 16, koff[i], 0, 0, 0);
     }
-#pragma unroll
-    for (int i = 0; i < C::vDmaPerWave; ++i) {
-      const int blk = wave + kF8Waves * i;
-      if (C::vDma % kF8Waves == 0 || blk < C::vDma)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(vbuf[B] + blk * 1024), 16, voff[i], 0, 0, 0);
-    }
-#endif
-#if defined(__HIP_DEVICE_COMPILE__)
     // K scales of keys k0.. (range-checked: keys past N read 0)
     const __amdgpu_buffer_rsrc_t rks = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(ksh + (int64_t)k0 * (D / 32)), (short)0, (N - k0) * (D / 32), 0x00020000);
@@ -325,34 +318,47 @@ struct FwdF8 {
       for (int kb = 0; kb < 2; ++kb)
         ksw[B][kb] = __builtin_amdgcn_raw_buffer_load_b16(rks, 2 * (32 * kb + l32), 0, 0);
     }
+#endif
+  }
+
+  // Queue the V^T tile at key k0 into buffer B: codes and scale words by
+  // LDS-DMA.
+  template <int B>
+  __device__ void issue_v(int k0) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(vth + (int64_t)(k0 / kF8Keys) * D * kF8Keys), (short)0, D * kF8Keys, 0x00020000);
+#pragma unroll
+    for (int i = 0; i < C::vDmaPerWave; ++i) {
+      const int blk = wave + kF8Waves * i;
+      if (C::vDma % kF8Waves == 0 || blk < C::vDma)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(vbuf[B] + blk * 1024), 16, voff[i], 0, 0, 0);
+    }
     // the tile's 64 V scale entries of D/32 bytes, one dword per lane (the
     // range ends with the head's last tile).  Every wave queues the same
     // scale words to the same place: the copies are identical, and a load
     // that depends on the wave would make the compiler wait for every load
     // in flight before each read of LDS.
-    {
-      const int off = (k0 / kF8Keys) * 64 * (D / 32);
-      const __amdgpu_buffer_rsrc_t rs =
-          __builtin_amdgcn_make_buffer_rsrc((void*)(vsh + off), (short)0, vs_bytes - off, 0x00020000);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)vsbuf[B], 4, 4 * (32 * hl + l32), 0, 0, 0);
-    }
+    const int off = (k0 / kF8Keys) * 64 * (D / 32);
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(vsh + off), (short)0, vs_bytes - off, 0x00020000);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)vsbuf[B], 4, 4 * (32 * hl + l32), 0, 0, 0);
 #endif
   }
 
-  template <bool MASK, int PAR>
-  __device__ void consume(int k0) {
-    const unsigned char* kt = kbuf[PAR];
-    const unsigned char* vt = vbuf[PAR];
-    f32x16 s[2];
+  // S^T = K Q^T of the K tile in buffer B.
+  template <int B>
+  __device__ __forceinline__ void scores(f32x16 (&s)[2]) {
+    const unsigned char* kt = kbuf[B];
     // d = 128: the scale words of key rows l32 and 32 + l32, adjacent in LDS
     u32x2 kw = {0u, 0u};
-    if constexpr (D == 128) kw = reinterpret_cast<const u32x2*>(ksbuf[PAR])[l32];
+    if constexpr (D == 128) kw = reinterpret_cast<const u32x2*>(ksbuf[B])[l32];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
       // scale word of this lane's key row: byte ks = block 2*ks + hl
-      const unsigned w = D == 128 ? kw[kb] : ksw[PAR][kb];
+      const unsigned w = D == 128 ? kw[kb] : ksw[B][kb];
       const unsigned ksc = __builtin_amdgcn_perm(w, w, ksel);
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
@@ -366,6 +372,11 @@ struct FwdF8 {
           s[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, qf[ks], s[kb], 0, 0, 1, (int)ksc, 1, qsc);
       }
     }
+  }
+
+  // Causal and tail masks of the tile at key k0, then the row max.
+  template <bool MASK>
+  __device__ __forceinline__ float masked_max(f32x16 (&s)[2], int k0) {
     if constexpr (MASK) {
       // key = k0 + 32*kb + (r&3) + 8*(r>>2) + 4*hl must be <= min(qi, N-1)
       const int lim = (CAUSAL ? min(qi, N - 1) : N - 1) - k0 - 4 * hl;
@@ -380,24 +391,27 @@ struct FwdF8 {
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = (kb == 0 ? 1 : 0); r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-    mx = max_across_halves(mx);
-    const bool upd = mx > m + thr;
-    if (__builtin_amdgcn_ballot_w64(upd)) {
-      asm volatile("" ::: "memory");   // keep this a taken/skipped branch
-      const float m_new = upd ? mx : m;
-      const float alpha = upd ? __builtin_amdgcn_exp2f((m - m_new) * c) : 1.f;
+    return max_across_halves(mx);
+  }
+
+  // Move the offset to the row max where it passed the offset by more than
+  // the lazy headroom, rescaling O and l by exp(m_old - m_new).
+  __device__ __forceinline__ void move_offset(float mx, bool upd) {
+    const float m_new = upd ? mx : m;
+    const float alpha = upd ? __builtin_amdgcn_exp2f((m - m_new) * c) : 1.f;
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
+      for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) lacc[r] *= alpha;
-      m = m_new;
-    }
+    for (int r = 0; r < 16; ++r) lacc[r] *= alpha;
+    m = m_new;
+  }
+
+  // P rounded to E4M3 against the current offset: byte 16*kb + r of the
+  // operand holds element r of score block kb.
+  __device__ __forceinline__ void probs(const f32x16 (&s)[2], i32x8& pf) {
     const float mc = m * c;
-    // P rounded to E4M3: byte 16*kb + r of the operand holds element r of
-    // score block kb
-    i32x8 pf;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -412,12 +426,20 @@ struct FwdF8 {
         word = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, word, true);
         pf[4 * kb + w] = word;
       }
+  }
+
+  // l += rowsum(P) (a ones-operand product over the rounded P, so the
+  // denominator sees exactly the numerator's weights) and O^T += V^T P^T
+  // with the V tile in buffer B.
+  template <int B>
+  __device__ __forceinline__ void pv(const i32x8& pf) {
     const i32x8 ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838,
                         0x38383838, 0x38383838, 0x38383838, 0x38383838};
     lacc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones, pf, lacc, 0, 0, 0, kUnitScale, 0, kUnitScale);
+    const unsigned char* vt = vbuf[B];
     const int ln = 32 * hl + l32;
-    const unsigned vsc = D == 128 ? reinterpret_cast<const unsigned*>(vsbuf[PAR])[ln]
-                                  : reinterpret_cast<const unsigned short*>(vsbuf[PAR])[ln];
+    const unsigned vsc = D == 128 ? reinterpret_cast<const unsigned*>(vsbuf[B])[ln]
+                                  : reinterpret_cast<const unsigned short*>(vsbuf[B])[ln];
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
       const unsigned char* src = vt + 32 * db * C::vStride;
@@ -435,24 +457,191 @@ struct FwdF8 {
     }
   }
 
+  // The end of a step: every load queued in it has landed (the builtin
+  // wait, which the compiler sees: it then does not wait for these loads
+  // again after the next tile's are queued) and every wave is done with the
+  // buffers the next step refills.  A VALU read of a
+  // v_mfma_scale_f32_32x32x64_f8f6f4 result needs 20 wait states on the
+  // MI355X (measured: at 19 the last result registers still hold their old
+  // values), one more than the compiler counts; four wait states after the
+  // barrier, which no product may be moved past, keep the first reads of
+  // the step's products far enough behind.
+  __device__ __forceinline__ void end_step() {
+    __builtin_amdgcn_s_waitcnt(0x0070u);   // vmcnt(0) lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_nop 3" ::: "memory");
+  }
+
+  // Normalise and store this lane's row: O = O~ / l as bf16, and
+  // LSE = scale m + ln l.
+  __device__ __forceinline__ void finish(unsigned short* orow, float* lrow, float scale) {
+    if (!orow) return;
+    const float l_tot = lacc[0];
+    const float inv = 1.f / l_tot;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int dim = 32 * db + 8 * g + 4 * hl;
+        const u32x2 w = {pack_bf16x2(acc[db][4 * g] * inv, acc[db][4 * g + 1] * inv),
+                         pack_bf16x2(acc[db][4 * g + 2] * inv, acc[db][4 * g + 3] * inv)};
+        *reinterpret_cast<u32x2*>(orow + dim) = w;
+      }
+    if (lrow) *lrow = m * scale + logf(l_tot);
+  }
+
+  // ---- d = 128: one tile per step -------------------------------------
+  // Queue tile j + 1 into buffers PAR ^ 1 (it gets the whole step to land),
+  // then the scores, softmax and products with V of tile j in buffers PAR.
+  // A wave whose last query precedes the tile's first key skips it (causal).
   template <bool MASK, int PAR>
   __device__ void step(int j, int t_end) {
     const int k0 = j * kF8Keys;
-    if (j + 1 < t_end) issue<PAR ^ 1>(k0 + kF8Keys);
-    if (!MASK || !CAUSAL || k0 <= qw + 31) consume<MASK, PAR>(k0);
-    // the builtin wait (vmcnt(0) lgkmcnt(0)), which the compiler sees: it
-    // then does not wait for these loads again after the next tile's are
-    // queued
-    __builtin_amdgcn_s_waitcnt(0x0070u);
-    __builtin_amdgcn_s_barrier();
-    // A VALU read of a v_mfma_scale_f32_32x32x64_f8f6f4 result needs 20 wait
-    // states on the MI355X (measured: at 19 the last result registers still
-    // hold their old values), one more than the compiler counts.  The
-    // register copies it places where the tile loops exit read the last
-    // tile's accumulators; these four wait states, which no product of the
-    // step may be moved past, keep such copies far enough behind.
+    if (j + 1 < t_end) {
+      issue_k<PAR ^ 1>(k0 + kF8Keys);
+      issue_v<PAR ^ 1>(k0 + kF8Keys);
+    }
+    if (!MASK || !CAUSAL || k0 <= qw + 31) {
+      f32x16 s[2];
+      scores<PAR>(s);
+      const float mx = masked_max<MASK>(s, k0);
+      const bool upd = mx > m + thr;
+      if (__builtin_amdgcn_ballot_w64(upd)) {
+        asm volatile("" ::: "memory");   // keep this a taken/skipped branch
+        move_offset(mx, upd);
+      }
+      i32x8 pf;
+      probs(s, pf);
+      pv<PAR>(pf);
+    }
+    end_step();
+  }
+
+  // ---- d = 64: three tiles in flight per step --------------------------
+  // At d = 64 a tile's vector work (exponentials, conversions, row max) is
+  // about twice its matrix work, so the step overlaps them within the
+  // wave: step j multiplies tile j - 1's probabilities with V, takes the
+  // scores of tile j + 1 and the softmax of tile j, three independent
+  // pieces, with the products placed one by one between runs of the
+  // vector work.  The probabilities are taken against the current offset
+  // before the offset test; when the row max passes the offset by more
+  // than the headroom, O and l are rescaled (after the product with tile
+  // j - 1's V, as in the serial order) and the probabilities taken again.
+  // Every kept value is the one the serial order gives.
+  static constexpr int kProducts = 1 + DB + 2 * KS;   // per step
+  static constexpr int kVectorRun = 7;                 // vector instructions after each product
+
+  template <bool MASK>
+  __device__ __forceinline__ void softmax_ahead(f32x16 (&s)[2], i32x8& pf, int k0) {
+    const float mx = masked_max<MASK>(s, k0);
+    probs(s, pf);
+    // one product, then two LDS reads (for a later product), then a run of
+    // vector instructions (exponentials included), kProducts times
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int i = 0; i < kProducts; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x402, kVectorRun, 0);
+    }
+    const bool upd = mx > m + thr;
+    if (__builtin_amdgcn_ballot_w64(upd)) {
+      // The products with V of the previous tile, issued just before, write
+      // the accumulators read here: 21 wait states first (see end_step).
+      __builtin_amdgcn_sched_barrier(0);
+      asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 4" ::: "memory");
+      move_offset(mx, upd);
+      probs(s, pf);
+    }
+  }
+
+  // Step j, PAR = j & 1: queue K of tile j + 2 and V of tile j into buffers
+  // PAR; then the product with V of tile j - 1 (probabilities pp, V in
+  // buffers PAR ^ 1), the scores of tile j + 1 (K in buffers PAR ^ 1, into
+  // sn) and the softmax of tile j (scores sc, probabilities into pc).
+  // PREV: tile j - 1 exists; NEXT: tile j + 1 exists.  Every wave does all
+  // three (a skipped piece would leave the products' accumulators in
+  // different registers on the two paths): the scores of a wave with no
+  // query at or after a tile's keys are all masked, its probabilities 0.
+  template <bool MASK, int PAR, bool PREV, bool NEXT>
+  __device__ void pstep(int j, int t_end, f32x16 (&sc)[2], f32x16 (&sn)[2], const i32x8& pp, i32x8& pc) {
+    const int k0 = j * kF8Keys;
+    if (j + 2 < t_end) issue_k<PAR>(k0 + 2 * kF8Keys);
+    issue_v<PAR>(k0);
+    if constexpr (PREV) pv<PAR ^ 1>(pp);
+    if constexpr (NEXT) scores<PAR ^ 1>(sn);
+    softmax_ahead<MASK>(sc, pc, k0);
+    end_step();
+  }
+
+  // The product with V of the last tile (buffers B), then 21 wait states
+  // before anything reads the accumulators.
+  template <int B>
+  __device__ void last_pv(const i32x8& pp) {
+    pv<B>(pp);
     __builtin_amdgcn_sched_barrier(0);
-    asm volatile("s_nop 3" ::: "memory");
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 4" ::: "memory");
+  }
+
+  // The last one or two tiles from tile j on (buffers P first), then the
+  // product with V of the last one.
+  template <int P>
+  __device__ void ptail(int j, int t_end, f32x16 (&sa)[2], f32x16 (&sb)[2], i32x8& pa, i32x8& pb) {
+    if (j + 1 < t_end) {
+      pstep<true, P, true, true>(j, t_end, sa, sb, pa, pb);
+      pstep<true, P ^ 1, true, false>(j + 1, t_end, sb, sa, pb, pa);
+      last_pv<P ^ 1>(pa);
+    } else {
+      pstep<true, P, true, false>(j, t_end, sa, sb, pa, pb);
+      last_pv<P>(pb);
+    }
+  }
+
+  // Tiles [0, full_end) need no mask and have a successor; the one or two
+  // after them are diagonal, ragged or last.  FP = full_end & 1 fixes every
+  // tile's buffer and register parity at compile time (one copy of the walk
+  // per parity: merging the two would leave the accumulators in different
+  // registers on the two paths, and the copies then spill).
+  template <int FP>
+  __device__ __forceinline__ void walk_pipelined(int n_tiles, int full_end, unsigned short* orow, float* lrow, float scale) {
+    f32x16 s0[2], s1[2];   // scores of the even and odd tiles
+    i32x8 p0, p1;          // their probabilities
+    // K of tiles 0 and 1, then the scores of tile 0; the barrier after them
+    // frees K buffer 0 for tile 2
+    issue_k<0>(0);
+    if (n_tiles > 1) issue_k<1>(kF8Keys);
+    __builtin_amdgcn_s_waitcnt(0x0070u);   // vmcnt(0) lgkmcnt(0)
+    __syncthreads();
+    scores<0>(s0);
+    __builtin_amdgcn_sched_barrier(0);
+    end_step();
+    if (FP == 0 && full_end == 0) {         // one or two tiles, both checked
+      if (n_tiles > 1) {
+        pstep<true, 0, false, true>(0, n_tiles, s0, s1, p1, p0);
+        pstep<true, 1, true, false>(1, n_tiles, s1, s0, p0, p1);
+        last_pv<1>(p1);
+      } else {
+        pstep<true, 0, false, false>(0, n_tiles, s0, s1, p1, p0);
+        last_pv<0>(p0);
+      }
+      finish(orow, lrow, scale);
+      return;
+    }
+    pstep<false, 0, false, true>(0, n_tiles, s0, s1, p1, p0);
+    int j = 1;
+    for (; j + 1 < full_end; j += 2) {
+      pstep<false, 1, true, true>(j, n_tiles, s1, s0, p0, p1);
+      pstep<false, 0, true, true>(j + 1, n_tiles, s0, s1, p1, p0);
+    }
+    if constexpr (FP == 0) {
+      pstep<false, 1, true, true>(j, n_tiles, s1, s0, p0, p1);
+      ++j;
+    }
+    // j == full_end, of parity FP
+    if constexpr (FP == 0) ptail<0>(j, n_tiles, s0, s1, p1, p0);
+    else                   ptail<1>(j, n_tiles, s1, s0, p0, p1);
+    finish(orow, lrow, scale);
   }
 };
 
@@ -560,38 +749,36 @@ __global__ __launch_bounds__(kF8Threads, 2) void fwd_fp8_kernel(
   const int n_tiles = (kv_end + kF8Keys - 1) / kF8Keys;
   const int n_full = CAUSAL ? min(q0 + 1, N) / kF8Keys : N / kF8Keys;
 
-  f.template issue<0>(0);
-  __builtin_amdgcn_s_waitcnt(0x0F70u);   // vmcnt(0)
-  __syncthreads();
-  int j = 0;
-  const int full_end = min(n_tiles, n_full);
-  for (; j + 1 < full_end; j += 2) {
-    f.template step<false, 0>(j, n_tiles);
-    f.template step<false, 1>(j + 1, n_tiles);
-  }
-  if (j < full_end) {
-    f.template step<false, 0>(j, n_tiles);
-    ++j;
-  }
-  for (; j < n_tiles; ++j) {
-    if (j & 1) f.template step<true, 1>(j, n_tiles);
-    else       f.template step<true, 0>(j, n_tiles);
-  }
-
-  if (!valid) return;
-  const float l_tot = f.lacc[0];
-  const float inv = 1.f / l_tot;
-  unsigned short* orow = o + qrow * D;
-#pragma unroll
-  for (int db = 0; db < F::DB; ++db)
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int dim = 32 * db + 8 * g + 4 * f.hl;
-      const u32x2 w = {pack_bf16x2(f.acc[db][4 * g] * inv, f.acc[db][4 * g + 1] * inv),
-                       pack_bf16x2(f.acc[db][4 * g + 2] * inv, f.acc[db][4 * g + 3] * inv)};
-      *reinterpret_cast<u32x2*>(orow + dim) = w;
+  unsigned short* orow = valid ? o + qrow * D : nullptr;
+  float* lrow = (valid && f.hl == 0) ? lse + qrow : nullptr;
+  if constexpr (D == 64) {
+    const int full_end = min(n_full, n_tiles - 1);
+    if (full_end & 1) f.template walk_pipelined<1>(n_tiles, full_end, orow, lrow, scale);
+    else              f.template walk_pipelined<0>(n_tiles, full_end, orow, lrow, scale);
+  } else {
+    // d = 128: one tile per step (the walk is written out here: as a member
+    // function the compiler kept the accumulators in two register sets at
+    // its exit and spilled)
+    f.template issue_k<0>(0);
+    f.template issue_v<0>(0);
+    __builtin_amdgcn_s_waitcnt(0x0F70u);   // vmcnt(0)
+    __syncthreads();
+    int j = 0;
+    const int full_end = min(n_tiles, n_full);
+    for (; j + 1 < full_end; j += 2) {
+      f.template step<false, 0>(j, n_tiles);
+      f.template step<false, 1>(j + 1, n_tiles);
     }
-  if (f.hl == 0) lse[qrow] = f.m * scale + logf(l_tot);
+    if (j < full_end) {
+      f.template step<false, 0>(j, n_tiles);
+      ++j;
+    }
+    for (; j < n_tiles; ++j) {
+      if (j & 1) f.template step<true, 1>(j, n_tiles);
+      else       f.template step<true, 0>(j, n_tiles);
+    }
+    f.finish(orow, lrow, scale);
+  }
 }
 
 template <int D>

@@ -55,7 +55,7 @@ def session(tmp_path, monkeypatch):
          _counter_rows("void at::native::copy_kernel(...)", "WRITE_SIZE", [262144.0] * 5))
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
     monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "profiles" / "traffic.json"))
-    monkeypatch.setattr(bench, "kernel_source_hash", lambda: "0123456789abcdef")
+    monkeypatch.setattr(bench, "kernel_source_hash", lambda names=None: "0123456789abcdef")
     return tmp_path, str(out)
 
 
@@ -80,7 +80,7 @@ def test_traffic_reported_only_for_the_same_source_and_workload(session, monkeyp
     bench.summarize(out, "wl")
     assert bench.measured_traffic("wl") == pytest.approx((810000.0 * 2.0 + 130000.0) * 1024)
     assert bench.measured_traffic("other") is None
-    monkeypatch.setattr(bench, "kernel_source_hash", lambda: "fedcba9876543210")
+    monkeypatch.setattr(bench, "kernel_source_hash", lambda names=None: "fedcba9876543210")
     assert bench.measured_traffic("wl") is None
 
 
@@ -91,6 +91,23 @@ def test_summary_keeps_other_workloads(session):
     t = json.load(open(str(tmp / "profiles" / "traffic.json")))
     assert set(t) == {"wl", "wl2"}
     assert bench.measured_traffic("wl2") == pytest.approx(bench.measured_traffic("wl"))
+
+
+def test_per_kernel_counters_average_a_counter_of_both_passes(session):
+    """GRBM_GUI_ACTIVE is collected in both counter passes of a path; with the
+    dispatch ids of the two runs alike, it is averaged, not summed."""
+    tmp, out = session
+    kern = "void fa::(anonymous namespace)::fwd_fp8_kernel<128, true>(...)"
+    hdr = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"]
+    _csv(os.path.join(out, "fp8_sq", "run_counter_collection.csv"), hdr,
+         _counter_rows(kern, "GRBM_GUI_ACTIVE", [8e6, 8e6]) + _counter_rows(kern, "SQ_VALU_MFMA_BUSY_CYCLES", [512e6, 512e6]))
+    _csv(os.path.join(out, "fp8_sq2", "run_counter_collection.csv"), hdr,
+         _counter_rows(kern, "GRBM_GUI_ACTIVE", [8e6, 8e6]) + _counter_rows(kern, "SQ_INSTS_MFMA", [1e6, 1e6]))
+    bench.summarize(out, "wl")
+    txt = open(str(tmp / "profiles" / "fa_fwd_fp8_bf16_n16k_d128_causal_amplified_counters.txt")).read()
+    assert "GRBM_GUI_ACTIVE              8e+06" in txt
+    # 512e6 busy cycles over (8e6 / 8 XCDs) cycles x 1024 SIMDs
+    assert "MFMA busy = 50.0 %" in txt
 
 
 def test_io_models_match_the_pages_formulas():

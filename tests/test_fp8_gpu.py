@@ -168,9 +168,19 @@ def _check_rows(O, L, deq, scale, causal, rows, what):
     assert np.all(el <= lb), what + ": LSE outside the derived bound"
 
 
+# At d = 64 the kernel walks the key tiles three at a time (the product with
+# V of tile j - 1, the softmax of tile j and the scores of tile j + 1 in one
+# step), with separate code for one or two tiles in all, for an odd or even
+# number of unmasked tiles, and for a tail of one or two tiles: the d = 64
+# shapes below take each of these.
 @pytest.mark.parametrize("B,H,N,d,causal", [(1, 2, 300, 64, True), (2, 2, 257, 128, False),
                                              (1, 1, 1000, 128, True), (1, 2, 64, 64, False),
-                                             (1, 1, 1, 128, True)])
+                                             (1, 1, 1, 128, True),
+                                             (1, 1, 1, 64, False), (1, 2, 40, 64, True),
+                                             (1, 2, 65, 64, True), (1, 1, 128, 64, False),
+                                             (1, 3, 129, 64, False), (2, 1, 192, 64, True),
+                                             (1, 1, 257, 64, True), (1, 2, 384, 64, False),
+                                             (1, 1, 449, 64, True)])
 def test_fp8_random_within_derived_bound(B, H, N, d, causal):
     torch_or_skip()
     case = "fp8 random B=%d H=%d N=%d d=%d causal=%d" % (B, H, N, d, causal)

@@ -62,7 +62,7 @@ def test_checker_refuses_an_unmeasured_product():
 
 def _assembly(src, out):
     from io_aware_softmax_fwd_amd import build as B
-    cmd = [B.HIPCC, *[f for f in B.DEVICE_FLAGS if f not in ("-fPIC",)], "-I", B.INCLUDE, "-I", CSRC,
+    cmd = [B.HIPCC, *[f for f in B.device_flags(src) if f not in ("-fPIC",)], "-I", B.INCLUDE, "-I", CSRC,
            "--cuda-device-only", "-S", os.path.join(CSRC, src), "-o", out]
     return subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True)
 
