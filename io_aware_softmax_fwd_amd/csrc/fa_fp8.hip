@@ -36,7 +36,11 @@
 // d = 128 walks the tiles one per step; d = 64, whose vector work is about
 // twice its matrix work, keeps three tiles in flight per step so that the
 // two overlap within a wave (FwdF8::walk_pipelined).
+// Small grids (a few heads of short sequences) run fwd_fp8_ws_kernel, whose
+// four waves split a 32-row block's key tiles between them.
 #include <math.h>
+
+#include <type_traits>
 
 #include "fa_device.h"
 #include "fa_internal.h"
@@ -781,6 +785,294 @@ __global__ __launch_bounds__(kF8Threads, 2) void fwd_fp8_kernel(
   }
 }
 
+// ------------------------------------------------------------ small grids
+// When the 128-row launch would leave most CUs idle (a few heads of short
+// sequences), the time is one workgroup's serial walk over all key tiles.
+// Here a workgroup takes 32 query rows and each of its four waves every
+// fourth key tile (wave w: tiles w, w+4, ...) through LDS slots of its own,
+// so a row's keys are covered by four independent online-softmax passes
+// that run side by side; their partial results (offset m, sum l and
+// unnormalised O) then meet in LDS and are merged as key chunks are
+// (LSE = log sum_w exp(LSE_w); zzszmyf.github.io notes, sections 5 and
+// 12.1), each wave writing a quarter of the head dims.  A wave refills its
+// K slot with its next tile once the scores have read it and its V slot
+// once the product with V has, so each load overlaps the other half of the
+// tile's work; the workgroups of a head first touch one share each of the
+// head's K and V lines, so that later tiles come from L2.
+constexpr int64_t kF8WsMaxGrid = 192;   // 128-row workgroups (3/4 of the CUs)
+constexpr int kF8WsMinTiles = 8;
+
+// s_waitcnt immediate: vmcnt n, lgkmcnt and expcnt not waited for (gfx9
+// layout: vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
+constexpr unsigned f8_wait_vm(int n) { return 0x0F70u | (unsigned)(n & 15) | ((unsigned)(n >> 4) & 3u) << 14; }
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kF8Threads, 2) void fwd_fp8_ws_kernel(
+    const unsigned char* __restrict__ q8, const unsigned char* __restrict__ qs,
+    const unsigned char* __restrict__ k8, const unsigned char* __restrict__ ks,
+    const unsigned char* __restrict__ v8t, const unsigned char* __restrict__ vs,
+    unsigned short* __restrict__ o, float* __restrict__ lse, int N, int BH, int n_qb, float scale,
+    int hg, int H, int G) {
+  using F = FwdF8<D, CAUSAL>;
+  using C = F8Cfg<D>;
+  // per wave: a K slot (codes, then the K scale words) and a V slot (codes,
+  // then the V scale words); afterwards they hold the wave's partial result
+  __shared__ __attribute__((aligned(1024))) unsigned char k_lds[kF8Waves][C::kTile + 256];
+  __shared__ __attribute__((aligned(1024))) unsigned char v_lds[kF8Waves][C::vTile + 256];
+  constexpr int BR = 32;
+  constexpr int kDma = C::kDma, vDma = C::vDma;
+  constexpr int nK = kDma + (D == 128 ? 1 : 2);   // loads of one K tile (codes, scales)
+  constexpr int nV = vDma + 1;                    // loads of one V tile
+  const int T = (N + kF8Keys - 1) / kF8Keys;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  int bh, rank;
+  xcd_order(blockIdx.x, BH, n_qb, hg, bh, rank);
+  const int q0 = (n_qb - 1 - rank) * BR;   // heaviest causal blocks first
+
+  F f;
+  unsigned char* const kt = k_lds[wave];
+  unsigned char* const vt = v_lds[wave];
+  f.kbuf[0] = kt;
+  f.ksbuf[0] = kt + C::kTile;
+  f.vbuf[0] = vt;
+  f.vsbuf[0] = vt + C::vTile;
+  const int64_t kvh = (int64_t)(bh / H) * (H / G) + (bh % H) / G;
+  f.kh = k8 + kvh * N * D;
+  f.ksh = ks + kvh * N * (D / 32);
+  f.vth = v8t + kvh * T * D * kF8Keys;
+  f.vsh = vs + kvh * T * 2 * 32 * (D / 32);
+  f.vs_bytes = T * 64 * (D / 32);
+  f.N = N;
+  f.wave = wave;
+  f.l32 = lane & 31;
+  f.hl = lane >> 5;
+  f.ksel = D == 128 ? (f.hl ? 0x0c0c0301u : 0x0c0c0200u) : (f.hl ? 0x0c0c0c01u : 0x0c0c0c00u);
+  f.qw = q0;                 // every wave holds the block's 32 rows
+  f.qi = q0 + f.l32;
+  f.c = scale * kLog2e;
+  f.thr = kF8Lazy / f.c;
+  f.m = -INFINITY;
+#pragma unroll
+  for (int db = 0; db < F::DB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) f.acc[db][r] = 0.f;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) f.lacc[r] = 0.f;
+  const bool valid = f.qi < N;
+  const int64_t qrow = (int64_t)bh * N + f.qi;
+#pragma unroll
+  for (int kk = 0; kk < F::KS; ++kk) {
+    u32x4 a0 = {0u, 0u, 0u, 0u}, a1 = {0u, 0u, 0u, 0u};
+    if (valid) {
+      const unsigned char* src = q8 + qrow * D + 64 * kk + 16 * f.hl;
+      a0 = *reinterpret_cast<const u32x4*>(src);
+      a1 = *reinterpret_cast<const u32x4*>(src + 32);
+    }
+    f.qf[kk] = __builtin_bit_cast(i32x8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
+  }
+  {
+    unsigned w = 0;
+    if (valid) {
+      if constexpr (D == 128) w = *reinterpret_cast<const unsigned*>(qs + qrow * 4);
+      else w = *reinterpret_cast<const unsigned short*>(qs + qrow * 2);
+    }
+    f.qsc = D == 128 ? (int)(((w >> (8 * f.hl)) & 0xFF) | (((w >> (16 + 8 * f.hl)) & 0xFF) << 8))
+                     : (int)((w >> (8 * f.hl)) & 0xFF);
+  }
+#pragma unroll
+  for (int ks2 = 0; ks2 < F::KS; ++ks2)
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      f.k_rd[2 * ks2 + h] = f.l32 * C::kStride + 16 * ((4 * ks2 + 2 * h + f.hl) ^ C::kswz(f.l32));
+#pragma unroll
+  for (int h = 0; h < 2; ++h) f.v_rd[h] = f.l32 * C::vStride + 16 * ((2 * f.hl + h) ^ C::vswz(f.l32));
+  // this wave loads whole tiles: LDS-DMA block i covers 16-byte slots
+  // 64 i .. 64 i + 63 of the tile
+  const auto kswz = [](int r) { return C::kswz(r); };
+  const auto vswz = [](int r) { return C::vswz(r); };
+  int koff[kDma], voff[vDma];
+#pragma unroll
+  for (int i = 0; i < kDma; ++i) koff[i] = f8_dma_offset(i * 64 + lane, C::KCH, kswz);
+#pragma unroll
+  for (int i = 0; i < vDma; ++i) voff[i] = f8_dma_offset(i * 64 + lane, C::VCH, vswz);
+  auto load_k = [&](int k0) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    const __amdgpu_buffer_rsrc_t rk =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(f.kh + (int64_t)k0 * D), (short)0, (N - k0) * D, 0x00020000);
+#pragma unroll
+    for (int i = 0; i < kDma; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(kt + i * 1024), 16, koff[i], 0, 0, 0);
+    const __amdgpu_buffer_rsrc_t rks = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(f.ksh + (int64_t)k0 * (D / 32)), (short)0, (N - k0) * (D / 32), 0x00020000);
+    if constexpr (D == 128) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rks, (lds_void*)f.ksbuf[0], 4,
+                                               4 * (32 * (f.l32 & 1) + 16 * f.hl + (f.l32 >> 1)), 0, 0, 0);
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+        f.ksw[0][kb] = __builtin_amdgcn_raw_buffer_load_b16(rks, 2 * (32 * kb + f.l32), 0, 0);
+    }
+#endif
+  };
+  auto load_v = [&](int k0) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(f.vth + (int64_t)(k0 / kF8Keys) * D * kF8Keys), (short)0, D * kF8Keys, 0x00020000);
+#pragma unroll
+    for (int i = 0; i < vDma; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(vt + i * 1024), 16, voff[i], 0, 0, 0);
+    const int off = (k0 / kF8Keys) * 64 * (D / 32);
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(f.vsh + off), (short)0, f.vs_bytes - off, 0x00020000);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)f.vsbuf[0], 4, 4 * (32 * f.hl + f.l32), 0, 0, 0);
+#endif
+  };
+
+  const int kv_end = CAUSAL ? min(N, q0 + BR) : N;
+  const int n_tiles = (kv_end + kF8Keys - 1) / kF8Keys;
+  const int n_full = CAUSAL ? min(q0 + 1, N) / kF8Keys : N / kF8Keys;
+
+  // One tile of this wave: its K and V were queued (K first), and loads
+  // return in order, so waiting until at most nV (nK) loads are outstanding
+  // means that the K (V) loads issued before them have landed.
+  auto tile = [&](auto mask, int j) {
+    constexpr bool MASK = decltype(mask)::value;
+    const int k0 = j * kF8Keys, jn = j + kF8Waves;
+    const bool more = jn < n_tiles;
+    __builtin_amdgcn_s_waitcnt(f8_wait_vm(nV));
+    f32x16 s[2];
+    f.template scores<0>(s);
+    __builtin_amdgcn_s_waitcnt(0xC07Fu);   // lgkmcnt(0): the K slot has been read
+    if (more) load_k(jn * kF8Keys);
+    const float mx = f.template masked_max<MASK>(s, k0);
+    const bool upd = mx > f.m + f.thr;
+    if (__builtin_amdgcn_ballot_w64(upd)) {
+      asm volatile("" ::: "memory");   // keep this a taken/skipped branch
+      f.move_offset(mx, upd);
+    }
+    i32x8 pf;
+    f.probs(s, pf);
+    if (more) __builtin_amdgcn_s_waitcnt(f8_wait_vm(nK));
+    else      __builtin_amdgcn_s_waitcnt(f8_wait_vm(0));
+    f.template pv<0>(pf);
+    __builtin_amdgcn_s_waitcnt(0xC07Fu);   // the V slot has been read
+    if (more) load_v(jn * kF8Keys);
+  };
+  // L2 warm-up: each workgroup of a head touches one share of the head's K
+  // code and V code lines (one dword per 128-byte line)
+  constexpr int kPrefetch = 2;
+  unsigned warm[kPrefetch];
+  {
+    const int64_t klines = ((int64_t)kv_end * D + 127) / 128;
+    const int64_t vlines = ((int64_t)((kv_end + kF8Keys - 1) / kF8Keys) * D * kF8Keys + 127) / 128;
+    const int64_t kper = (klines + n_qb - 1) / n_qb, vper = (vlines + n_qb - 1) / n_qb;
+    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)f.kh, (short)0, N * D, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rv =
+        __builtin_amdgcn_make_buffer_rsrc((void*)f.vth, (short)0, T * D * kF8Keys, 0x00020000);
+#pragma unroll
+    for (int i = 0; i < kPrefetch; ++i) {
+      const int64_t e = (int64_t)i * kF8Threads + tid;
+      warm[i] = 0u;
+      if (e < kper) {
+        const int64_t line = (int64_t)rank * kper + e;
+        if (line < klines) warm[i] = __builtin_amdgcn_raw_buffer_load_b32(rk, (int)(line * 128), 0, 0);
+      } else if (e < kper + vper) {
+        const int64_t line = (int64_t)rank * vper + (e - kper);
+        if (line < vlines) warm[i] = __builtin_amdgcn_raw_buffer_load_b32(rv, (int)(line * 128), 0, 0);
+      }
+    }
+  }
+  int j = wave;
+  if (j < n_tiles) {
+    load_k(j * kF8Keys);
+    load_v(j * kF8Keys);
+    for (; j < min(n_full, n_tiles); j += kF8Waves) tile(std::false_type{}, j);
+    for (; j < n_tiles; j += kF8Waves) tile(std::true_type{}, j);
+  }
+  {
+    unsigned x = 0u;
+#pragma unroll
+    for (int i = 0; i < kPrefetch; ++i) x ^= warm[i];
+    asm volatile("" ::"v"(x));
+  }
+  __builtin_amdgcn_s_waitcnt(0x0070u);   // vmcnt(0) lgkmcnt(0)
+  // 21 wait states before the accumulators of the last products are read
+  // (a VALU read of a v_mfma_scale_f32_32x32x64_f8f6f4 result needs 20)
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 4" ::: "memory");
+  __syncthreads();
+
+  // Partial results to LDS: the unnormalised O^T of the wave as fp32
+  // [32 rows][D/2] per half of the head dims, the first half in its K slot
+  // and the second in its V slot (16-byte chunk c of a row at c ^ (row mod
+  // D/8)), its offsets and row sums after them.
+  constexpr int HC = D / 8;   // 16-byte chunks per row of a half
+  {
+#pragma unroll
+    for (int db = 0; db < F::DB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int c = 8 * db + 2 * g + f.hl;    // chunk of dims 32 db + 8 g + 4 hl
+        float* ob = reinterpret_cast<float*>(c < HC ? kt : vt);
+        const float4 w = {f.acc[db][4 * g], f.acc[db][4 * g + 1], f.acc[db][4 * g + 2], f.acc[db][4 * g + 3]};
+        *reinterpret_cast<float4*>(ob + f.l32 * (D / 2) + 4 * ((c % HC) ^ (f.l32 % HC))) = w;
+      }
+    if (f.hl == 0) {
+      reinterpret_cast<float*>(kt + C::kTile)[f.l32] = f.m;
+      reinterpret_cast<float*>(vt + C::vTile)[f.l32] = f.lacc[0];
+    }
+  }
+  __syncthreads();
+
+  // Merge: wave w writes head dims [w D/4, (w+1) D/4) of the 32 rows; lane
+  // (row, half) takes D/8 of them.  Key 0 is visible to every row and sits
+  // in wave 0's first tile, so the row max M is finite; a wave that saw no
+  // key of a row (offset -inf) weighs 0.
+  const int row = lane & 31, hh = lane >> 5;
+  constexpr int NC = D / 32;                   // 16-byte chunks per lane
+  float mw[kF8Waves], M = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < kF8Waves; ++w) {
+    mw[w] = reinterpret_cast<const float*>(k_lds[w] + C::kTile)[row];
+    M = fmaxf(M, mw[w]);
+  }
+  float L = 0.f;
+  float out[4 * NC];
+#pragma unroll
+  for (int e = 0; e < 4 * NC; ++e) out[e] = 0.f;
+  const int c0 = wave * (D / 16) + hh * NC;   // first chunk of this lane
+#pragma unroll
+  for (int w = 0; w < kF8Waves; ++w) {
+    const float a = mw[w] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((mw[w] - M) * f.c);
+    L += a * reinterpret_cast<const float*>(v_lds[w] + C::vTile)[row];
+    const float* ob = reinterpret_cast<const float*>(c0 < HC ? k_lds[w] : v_lds[w]);
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const int cc = (c0 + c) % HC;
+      const float4 x = *reinterpret_cast<const float4*>(ob + row * (D / 2) + 4 * (cc ^ (row % HC)));
+      out[4 * c] += a * x.x;
+      out[4 * c + 1] += a * x.y;
+      out[4 * c + 2] += a * x.z;
+      out[4 * c + 3] += a * x.w;
+    }
+  }
+  if (q0 + row >= N) return;
+  const int64_t grow = (int64_t)bh * N + q0 + row;
+  const float inv = 1.f / L;
+  unsigned short* orow = o + grow * D + 4 * c0;
+#pragma unroll
+  for (int c = 0; c < NC; c += 2) {
+    const u32x4 w = {pack_bf16x2(out[4 * c] * inv, out[4 * c + 1] * inv),
+                     pack_bf16x2(out[4 * c + 2] * inv, out[4 * c + 3] * inv),
+                     pack_bf16x2(out[4 * c + 4] * inv, out[4 * c + 5] * inv),
+                     pack_bf16x2(out[4 * c + 6] * inv, out[4 * c + 7] * inv)};
+    *reinterpret_cast<u32x4*>(orow + 4 * c) = w;
+  }
+  if (wave == 0 && hh == 0) lse[grow] = M * scale + logf(L);
+}
+
 template <int D>
 hipError_t launch_quant_rows(const void* x, int64_t rows, void* x8, void* xs, hipStream_t stream) {
   const int64_t threads = rows * (D / 32);
@@ -814,6 +1106,16 @@ template <int D, bool CAUSAL>
 hipError_t launch_fp8(const Fp8Problem& p, hipStream_t stream) {
   const int BH = p.B * p.H;
   const int n_qtiles = (p.N + 32 * kF8Waves - 1) / (32 * kF8Waves);
+  if ((int64_t)n_qtiles * BH <= kF8WsMaxGrid && (p.N + kF8Keys - 1) / kF8Keys >= kF8WsMinTiles) {
+    const int n_qb = (p.N + 31) / 32;
+    hipLaunchKernelGGL((fwd_fp8_ws_kernel<D, CAUSAL>), dim3((unsigned)((int64_t)n_qb * BH)), dim3(kF8Threads), 0,
+                       stream, static_cast<const unsigned char*>(p.q8), static_cast<const unsigned char*>(p.qs),
+                       static_cast<const unsigned char*>(p.k8), static_cast<const unsigned char*>(p.ks),
+                       static_cast<const unsigned char*>(p.v8t), static_cast<const unsigned char*>(p.vs),
+                       static_cast<unsigned short*>(p.o), p.lse, p.N, BH, n_qb, p.scale,
+                       xcd_head_group(BH, n_qb, 1, CAUSAL ? n_qb : 0, 1, 4), p.H, p.H / p.Hkv);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL((fwd_fp8_kernel<D, CAUSAL>), dim3((unsigned)((int64_t)n_qtiles * BH)),
                      dim3(kF8Threads), 0, stream, static_cast<const unsigned char*>(p.q8),
                      static_cast<const unsigned char*>(p.qs), static_cast<const unsigned char*>(p.k8),

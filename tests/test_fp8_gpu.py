@@ -172,7 +172,10 @@ def _check_rows(O, L, deq, scale, causal, rows, what):
 # V of tile j - 1, the softmax of tile j and the scores of tile j + 1 in one
 # step), with separate code for one or two tiles in all, for an odd or even
 # number of unmasked tiles, and for a tail of one or two tiles: the d = 64
-# shapes below take each of these.
+# shapes below take each of these.  Calls of at most 192 workgroups of 128
+# rows with at least 8 key tiles (N > 448) run the small-grid kernel instead
+# (32-row workgroups whose waves split the keys): the shapes with N >= 449
+# and few heads take it, (1, 48, 1000, 64, True) the walk above.
 @pytest.mark.parametrize("B,H,N,d,causal", [(1, 2, 300, 64, True), (2, 2, 257, 128, False),
                                              (1, 1, 1000, 128, True), (1, 2, 64, 64, False),
                                              (1, 1, 1, 128, True),
@@ -180,7 +183,9 @@ def _check_rows(O, L, deq, scale, causal, rows, what):
                                              (1, 2, 65, 64, True), (1, 1, 128, 64, False),
                                              (1, 3, 129, 64, False), (2, 1, 192, 64, True),
                                              (1, 1, 257, 64, True), (1, 2, 384, 64, False),
-                                             (1, 1, 449, 64, True)])
+                                             (1, 1, 449, 64, True), (2, 2, 520, 128, False),
+                                             (1, 3, 700, 64, False), (2, 1, 513, 64, True),
+                                             (1, 48, 1000, 64, True)])
 def test_fp8_random_within_derived_bound(B, H, N, d, causal):
     torch_or_skip()
     case = "fp8 random B=%d H=%d N=%d d=%d causal=%d" % (B, H, N, d, causal)
@@ -234,9 +239,10 @@ def test_fp8_workload_shapes(cfg):
     _check_rows(O, L, deq, w.scale, w.causal, rows, "C%d" % cfg)
 
 
+@pytest.mark.parametrize("H", [2, 64])   # the small-grid kernel, the 128-row kernel
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
-def test_fp8_offset_moves(d, causal):
+def test_fp8_offset_moves(d, causal, H):
     """Keys whose score against every query sits far above all earlier keys
     (by 69, 173 and 231 log2 units; one on the ragged last tile) and one far
     below: the row max passes the exponent offset by far more than the
@@ -244,8 +250,8 @@ def test_fp8_offset_moves(d, causal):
     the accumulators are rescaled before the probabilities are rounded to
     E4M3."""
     torch_or_skip()
-    H, N = 2, 700
-    case = "fp8 offset moves N=%d d=%d causal=%d" % (N, d, causal)
+    N = 700
+    case = "fp8 offset moves H=%d N=%d d=%d causal=%d" % (H, N, d, causal)
     note(case)
     rng = np.random.default_rng(9300 + d + causal)
     q = rng.standard_normal((1, H, N, d), dtype=np.float32) * 0.5
@@ -264,7 +270,8 @@ def test_fp8_offset_moves(d, causal):
     _check_rows(O, L, deq, 1.0, causal, np.arange(H * N), case)
 
 
-@pytest.mark.parametrize("B,H,Hkv,N,d,causal", [(1, 8, 2, 300, 128, True), (2, 4, 1, 257, 64, False)])
+@pytest.mark.parametrize("B,H,Hkv,N,d,causal", [(1, 8, 2, 300, 128, True), (2, 4, 1, 257, 64, False),
+                                                 (1, 4, 1, 600, 64, True)])
 def test_fp8_grouped_kv_heads(B, H, Hkv, N, d, causal):
     """fa_fwd_fp8_gqa: query head h reads K/V head h / (H/Hkv).  Against the
     oracle on the dequantized inputs with K/V repeated per query head, and bit
