@@ -190,28 +190,48 @@ __global__ __launch_bounds__(256) void quant_rows_rot_kernel(const unsigned shor
   }
 }
 
-// One thread per (head, tile, key block b, head dim c): the 32 keys
-// 64t + 32b .. +31 of dim c.  Their codes go to two 16-byte runs of tile row
-// c: positions 16b .. 16b+15 (keys with bit 2 of the key index clear) and
-// 32 + 16b .. (bit 2 set), in the accumulator key order.
+// One workgroup per 256 / (2 D) tiles (64 keys of one head): the tiles'
+// key rows are read from HBM as whole 16-byte chunks into LDS, then one
+// thread per (tile, key block b, head dim c) takes the 32 keys
+// 64t + 32b .. +31 of dim c from LDS.  Their codes go to two 16-byte runs
+// of tile row c: positions 16b .. 16b+15 (keys with bit 2 of the key index
+// clear) and 32 + 16b .. (bit 2 set), in the accumulator key order.  Keys
+// past N read 0.
 template <int D>
 __global__ __launch_bounds__(256) void quant_v_kernel(const unsigned short* __restrict__ v, int BH, int N,
                                                      int T, unsigned char* __restrict__ v8t,
                                                      unsigned char* __restrict__ vs) {
-  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (t >= (int64_t)BH * T * 2 * D) return;
-  const int c = (int)(t % D);
-  const int b = (int)((t / D) % 2);
-  const int64_t tile = t / (2 * D);            // bh * T + tile index
-  const int bh = (int)(tile / T);
-  const int k0 = (int)(tile % T) * kF8Keys + 32 * b;
-  const unsigned short* col = v + ((int64_t)bh * N) * D + c;
+  constexpr int TPB = 256 / (2 * D);           // tiles per workgroup
+  constexpr int CPR = D / 8;                   // 16-byte chunks per key row
+  __shared__ __attribute__((aligned(16))) unsigned short rows[TPB * kF8Keys * D];
+  const int64_t ntiles = (int64_t)BH * T;
+  const int64_t tile0 = (int64_t)blockIdx.x * TPB;
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < TPB * kF8Keys * CPR / 256; ++i) {
+    const int q = i * 256 + tid;               // chunk of the workgroup's rows
+    const int tl = q / (kF8Keys * CPR), key = (q / CPR) % kF8Keys, ch = q % CPR;
+    const int64_t tile = tile0 + tl;
+    u32x4 x = {0u, 0u, 0u, 0u};
+    if (tile < ntiles) {
+      const int bh = (int)(tile / T);
+      const int kg = (int)(tile % T) * kF8Keys + key;
+      if (kg < N) x = *reinterpret_cast<const u32x4*>(v + ((int64_t)bh * N + kg) * D + 8 * ch);
+    }
+    *reinterpret_cast<u32x4*>(rows + (tl * kF8Keys + key) * D + 8 * ch) = x;
+  }
+  __syncthreads();
+  const int c = tid % D;
+  const int b = (tid / D) % 2;
+  const int tl = tid / (2 * D);
+  const int64_t tile = tile0 + tl;            // bh * T + tile index
+  if (tile >= ntiles) return;
+  const unsigned short* col = rows + (tl * kF8Keys + 32 * b) * D + c;
   float val[32];
   unsigned amax = 0;
 #pragma unroll
   for (int r = 0; r < 32; ++r) {
-    const int key = k0 + r;
-    const unsigned short bits = key < N ? col[(int64_t)key * D] : (unsigned short)0;
+    const unsigned short bits = col[r * D];
     val[r] = bf16_to_f32(bits);
     amax = max(amax, ((unsigned)bits << 16) & 0x7FFFFFFFu);
   }
@@ -1095,8 +1115,9 @@ hipError_t launch_quant_rows_rot(const void* x, int64_t rows, const void* signs,
 template <int D>
 hipError_t launch_quant_v(const void* v, int BH, int N, void* v8t, void* vs, hipStream_t stream) {
   const int T = (N + kF8Keys - 1) / kF8Keys;
-  const int64_t threads = (int64_t)BH * T * 2 * D;
-  hipLaunchKernelGGL((quant_v_kernel<D>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream,
+  const int64_t tiles = (int64_t)BH * T;
+  constexpr int TPB = 256 / (2 * D);
+  hipLaunchKernelGGL((quant_v_kernel<D>), dim3((unsigned)((tiles + TPB - 1) / TPB)), dim3(256), 0, stream,
                      static_cast<const unsigned short*>(v), BH, N, T, static_cast<unsigned char*>(v8t),
                      static_cast<unsigned char*>(vs));
   return hipGetLastError();
